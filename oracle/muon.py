@@ -1,0 +1,146 @@
+"""Float64 reference of one Muon optimizer step (test infrastructure only).
+
+Every function takes and returns float64 NumPy arrays.  Inputs are upcast
+exactly from whatever the GPU receives (float32 or bfloat16 values), so the only
+rounding in here is float64 rounding.  Nothing is blocked, fused or reordered
+beyond what the cited definitions state; matrix products use NumPy's ``@``.
+
+Readings taken where the pages leave a step open (each is listed, with its
+reason, in the design notes of the repository):
+
+* Nesterov uses the *updated* buffer: the blog's VanillaMuon updates ``buf``
+  before forming the update, and the training guide defines the Nesterov input
+  as ``grad + mu * buf``.
+* The normalisation epsilon is added to the Frobenius norm (the blog's code
+  divides by ``norm + 1e-7``; its equation shows no epsilon).
+* Transposition happens strictly when rows > cols.
+* Matrices with fewer than 100,000 elements skip Newton-Schulz and use the
+  momentum input directly, as the blog's VanillaMuon does for non-matrix
+  parameters and as the training guide's predicate excludes them from NS.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+# Blog post, section "代码实现": the normalisation divides by (norm + 1e-7).
+EPS = 1e-7
+# Training guide, section "编写 Predicate": p.numel() < 100_000 is "too small,
+# NS has no benefit".
+MIN_NS_NUMEL = 100_000
+
+
+def _f64_2d(a) -> np.ndarray:
+    a = np.asarray(a, dtype=np.float64)
+    if a.ndim != 2:
+        # Blog post, section "常见错误" (mistake 2): NS is only defined on 2-D
+        # matrices; a bias vector must be rejected.
+        raise ValueError(f"expected a 2-D matrix, got shape {a.shape}")
+    return a
+
+
+def frobenius_norm(x: np.ndarray) -> float:
+    """sqrt of the sum of squares of all entries (the ||G||_F of the blog's
+    normalisation equation)."""
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.sqrt(np.sum(x * x)))
+
+
+def newton_schulz(g, steps: int) -> np.ndarray:
+    """Cubic Newton-Schulz orthogonalisation.
+
+    Blog post, section "Muon 核心：Newton-Schulz 迭代": G0 = G / ||G||_F, then
+    G_{t+1} = 1.5 G_t - 0.5 G_t G_t^T G_t, evaluated as two products per step
+    (A = G G^T, then A G).  Section "代码实现" (``newton_schulz``) fixes the
+    details: rows > cols is handled on the transpose so the Gram matrix is the
+    smaller side, and the norm gets +1e-7.
+    """
+    g = _f64_2d(g)
+    if steps < 0:
+        raise ValueError("steps must be >= 0")
+    rows, cols = g.shape
+    transposed = rows > cols
+    x = g.T if transposed else g
+    x = x / (frobenius_norm(x) + EPS)
+    for _ in range(steps):
+        a = x @ x.T
+        x = 1.5 * x - 0.5 * (a @ x)
+    return x.T if transposed else x
+
+
+def momentum_update(buf, grad, mu: float) -> np.ndarray:
+    """buf <- mu * buf + grad (blog post, ``VanillaMuon.step``: mul_ then add_)."""
+    return mu * np.asarray(buf, dtype=np.float64) + np.asarray(grad, dtype=np.float64)
+
+
+def ns_input(grad, buf_new, mu: float, nesterov: bool) -> np.ndarray:
+    """Matrix fed to Newton-Schulz.
+
+    Training guide, hyper-parameter table, ``nesterov``: ns_input = grad + mu * buf
+    (with the buffer already updated this step).  Without Nesterov the buffer
+    itself is used, as in the blog's VanillaMuon.
+    """
+    buf_new = np.asarray(buf_new, dtype=np.float64)
+    if nesterov:
+        return np.asarray(grad, dtype=np.float64) + mu * buf_new
+    return buf_new
+
+
+def muon_direction(y, steps: int) -> np.ndarray:
+    """Update direction U for one matrix: NS(y), or y itself when the matrix is
+    below the NS size threshold (blog VanillaMuon's non-matrix branch applied
+    to the training guide's numel < 100,000 exclusion)."""
+    y = _f64_2d(y)
+    if y.size < MIN_NS_NUMEL:
+        return y.copy()
+    return newton_schulz(y, steps)
+
+
+def apply_update(p, u, lr: float, lr_scale: float = 1.0) -> np.ndarray:
+    """p <- p - lr * scale * U (blog VanillaMuon: p.add_(update, alpha=-lr))."""
+    return np.asarray(p, dtype=np.float64) - (lr * lr_scale) * np.asarray(u, dtype=np.float64)
+
+
+def moonlight_lr_scale(rows: int, cols: int) -> float:
+    """Per-parameter learning-rate multiplier 0.2 * sqrt(max(m, n)) named in the
+    training guide's hyper-parameter table (``lr`` row)."""
+    return 0.2 * float(np.sqrt(max(rows, cols)))
+
+
+def muon_step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], bufs: Sequence[np.ndarray],
+              mu: float, nesterov: bool, steps: int, lr: float,
+              lr_scale: Optional[Sequence[float]] = None
+              ) -> Tuple[list, list, list, list]:
+    """One Muon step over a list of matrices, each independent of the others.
+
+    Returns (new_params, new_bufs, updates, norms) where ``updates`` are the U
+    matrices (in each parameter's own orientation) and ``norms`` are
+    ||ns_input||_F per matrix.
+    """
+    out_p, out_b, out_u, norms = [], [], [], []
+    for i, (p, g, b) in enumerate(zip(params, grads, bufs)):
+        g = _f64_2d(g)
+        b_new = momentum_update(b, g, mu)
+        y = ns_input(g, b_new, mu, nesterov)
+        u = muon_direction(y, steps)
+        s = 1.0 if lr_scale is None else float(lr_scale[i])
+        out_p.append(apply_update(p, u, lr, s))
+        out_b.append(b_new)
+        out_u.append(u)
+        norms.append(frobenius_norm(y))
+    return out_p, out_b, out_u, norms
+
+
+def orthogonality_error(x) -> float:
+    """||X X^T - I||_F, taken on the wide orientation of X.
+
+    Blog post, section "调试技巧" (``check_orthogonality``): the error of an
+    orthogonalised update.  For a tall X, X X^T has rank < rows and the error
+    could never approach 0, so the product is formed on the side with fewer
+    rows.
+    """
+    x = _f64_2d(x)
+    if x.shape[0] > x.shape[1]:
+        x = x.T
+    return frobenius_norm(x @ x.T - np.eye(x.shape[0]))

@@ -1,0 +1,105 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+The mutants live here, on the CPU; the oracle itself is untouched.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import _pins
+
+EPS = 1e-7
+
+
+def _ns_factory(norm=None, eps_inside=False, no_eps=False, c1=1.5, c2=0.5, gram="xxt",
+                steps_off=0, transpose_back=True):
+    def ns(g, steps):
+        g = np.asarray(g, dtype=np.float64)
+        if g.ndim != 2:
+            raise ValueError
+        m, n = g.shape
+        t = m > n
+        x = g.T if t else g
+        ss = float(np.sum(x * x))
+        if norm == "maxabs":
+            d = float(np.max(np.abs(x))) + EPS
+        elif norm == "spectral":
+            d = float(np.linalg.norm(x, 2)) + EPS
+        elif no_eps:
+            d = np.sqrt(ss)
+        elif eps_inside:
+            d = np.sqrt(ss + EPS)
+        else:
+            d = np.sqrt(ss) + EPS
+        with np.errstate(invalid="ignore", divide="ignore"):
+            x = x / d
+        for _ in range(max(steps + steps_off, 0)):
+            a = x.T @ x if gram == "xtx" else x @ x.T
+            if gram == "xtx":
+                x = c1 * x - c2 * (a @ x) if a.shape[0] == x.shape[0] else c1 * x - c2 * (x @ a.T @ a) / 1.0
+            else:
+                x = c1 * x - c2 * (a @ x)
+        return x.T if (t and transpose_back) else x
+    return ns
+
+
+NS_MUTANTS = {
+    "no_eps": _ns_factory(no_eps=True),
+    "eps_inside_sqrt": _ns_factory(eps_inside=True),
+    "maxabs_norm": _ns_factory(norm="maxabs"),
+    "spectral_norm": _ns_factory(norm="spectral"),
+    "coef_1.4": _ns_factory(c1=1.4),
+    "sign_flip": _ns_factory(c2=-0.5),
+    "half_coef_0.25": _ns_factory(c2=0.25),
+    "gram_transposed": _ns_factory(gram="xtx"),
+    "one_step_short": _ns_factory(steps_off=-1),
+    "one_step_long": _ns_factory(steps_off=1),
+    "no_transpose_back": _ns_factory(transpose_back=False),
+}
+
+
+def _fails_some_pin(ns):
+    for pin in _pins.NS_PINS:
+        try:
+            pin(ns)
+        except (AssertionError, ValueError, np.linalg.LinAlgError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(NS_MUTANTS))
+def test_ns_mutant_is_caught(name):
+    assert _fails_some_pin(NS_MUTANTS[name]), f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes():
+    assert not _fails_some_pin(_ns_factory())
+
+
+def _caught(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_momentum_mutants_are_caught(golden):
+    fixture = golden("momentum_worked_example.txt")
+    damped = lambda b, g, mu: mu * np.asarray(b) + (1 - mu) * np.asarray(g)  # noqa: E731
+    old_buf_nesterov = lambda g, b, mu, nest: (np.asarray(g) + mu * (np.asarray(b) - np.asarray(g)) / mu  # noqa: E731
+                                                if nest else np.asarray(b))
+    assert _caught(lambda: _pins.pin_geometric_series(damped, oracle.ns_input))
+    assert _caught(lambda: _pins.pin_two_step(oracle.momentum_update, old_buf_nesterov))
+
+    def step_with_mutant(mutant):
+        def muon_step(params, grads, bufs, mu, nesterov, steps, lr, lr_scale=None):
+            b = [mutant(bb, g, mu) for bb, g in zip(bufs, grads)]
+            y = [oracle.ns_input(g, bb, mu, nesterov) for g, bb in zip(grads, b)]
+            return [oracle.apply_update(p, yy, lr) for p, yy in zip(params, y)], b, y, None
+        return muon_step
+    assert _caught(lambda: _pins.pin_worked_example(step_with_mutant(damped), fixture))
+
+    off_by_one_route = lambda y, k: (np.asarray(y) if np.asarray(y).size <= 100_000  # noqa: E731
+                                     else oracle.newton_schulz(y, k))
+    assert _caught(lambda: _pins.pin_route_threshold(off_by_one_route, oracle.newton_schulz))
