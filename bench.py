@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark: one batched Muon step over a Llama-3-8B-shaped matrix set on one
+MI355X.
+
+A step is one dmuon_muon_step call over all 224 projection matrices
+(32 layers x q, k, v, o, gate, up, down): momentum + Nesterov + Frobenius norm,
+5 Newton-Schulz iterations (Gram product + update product per iteration) and
+the weight update.  Inputs are seeded synthetic tensors already resident in
+HBM: bf16 gradients ~ N(0, 1e-3^2), bf16 weights ~ N(0, 1), fp32 momentum
+starting at zero.
+
+Prints one JSON line.  `value` is the whole step's algorithmic Newton-Schulz
+throughput (TFLOP/s): per matrix and iteration m'(m'+1)n' for the
+lower-triangle Gram product plus 2m'^2 n' + 3m'n' for the update product and
+its epilogue (m' = min(rows, cols), n' = max(rows, cols)), divided by the
+measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def ns_flops(shapes, ns_steps):
+    syrk = gemm = 0.0
+    for r, c in shapes:
+        if r * c < 100_000:
+            continue
+        m, n = float(min(r, c)), float(max(r, c))
+        syrk += m * (m + 1.0) * n
+        gemm += 2.0 * m * m * n + 3.0 * m * n
+    return syrk * ns_steps, gemm * ns_steps
+
+
+def cpu_baseline(cfg, sample_idx, ns_steps, mu, lr):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    mats = []
+    for i in sample_idx:
+        g = gen.draw_matrix(cfg, i, gen.GRAD).as_f64()
+        p = gen.draw_matrix(cfg, i, gen.WEIGHT).as_f64()
+        mats.append((p, g, np.zeros_like(g)))
+    t0 = time.perf_counter()
+    for p, g, b in mats:
+        oracle.muon_step([p], [g], [b], mu, True, ns_steps, lr)
+    dt = time.perf_counter() - t0
+    shapes = [(cfg.matrices[i].rows, cfg.matrices[i].cols) for i in sample_idx]
+    s, g = ns_flops(shapes, ns_steps)
+    desc = ", ".join(f"{cfg.matrices[i].name} {cfg.matrices[i].rows}x{cfg.matrices[i].cols}" for i in sample_idx)
+    return {"value": (s + g) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one Muon step (k={ns_steps}) of {len(sample_idx)} matrices: {desc}; {dt:.2f} s wall, "
+                      f"float64 NumPy oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="llama3_8b")
+    ap.add_argument("--ns-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true", default=True)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the batched step runs the whole "
+              "matrix set on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import newton_schulz_08_amd as nsa
+    from workloads import get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = get_config(args.config)
+    ns_steps = args.ns_steps if args.ns_steps is not None else cfg.ns_steps[0]
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[cfg.dtype]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_setup = time.perf_counter()
+    gen_ = torch.Generator(device=dev)
+    gen_.manual_seed(42)
+    params, grads, moms = [], [], []
+    for spec in cfg.matrices:
+        shape = (spec.rows, spec.cols)
+        g = torch.randn(shape, generator=gen_, device=dev, dtype=torch.float32)
+        if cfg.grad_dist == "student_t3":
+            # t_3 = Z / sqrt(chi2_3 / 3)
+            chi = torch.randn((3,) + shape, generator=gen_, device=dev).pow_(2).sum(0).div_(3.0).sqrt_()
+            g.div_(chi)
+            del chi
+        g.mul_(cfg.grad_scale)
+        grads.append(g.to(dt))
+        del g
+        params.append((torch.randn(shape, generator=gen_, device=dev) * cfg.weight_scale).to(dt))
+        moms.append(torch.zeros(shape, device=dev, dtype=torch.float32))
+    step = nsa.MuonStep(params, grads, moms, ns_steps=ns_steps, mu=cfg.momentum, nesterov=cfg.nesterov, lr=cfg.lr)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print(f"[bench] {cfg.key}: {cfg.count} matrices, workspace {step.workspace_bytes / 2**30:.1f} GiB, "
+          f"setup {setup_s:.1f} s", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    nsa.profile_read()
+    if args.profile:
+        nsa.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nsa.profile_enable(False)
+    kstats = nsa.profile_read() if args.profile else {}
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    shapes = [(m.rows, m.cols) for m in cfg.matrices]
+    syrk_f, gemm_f = ns_flops(shapes, ns_steps)
+    ns_total = syrk_f + gemm_f
+    value = ns_total / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+
+    kernels = {}
+    for name, s in kstats.items():
+        avg_ms = s["total_ms"] / max(s["launches"], 1)
+        ent = {"launches": s["launches"], "avg_ms": avg_ms, "ms_per_step": s["total_ms"] / args.steps}
+        if s["flops"] > 0:
+            ent["tflops"] = s["flops"] / (s["total_ms"] * 1e-3) / 1e12
+        if s["bytes"] > 0:
+            ent["gbs"] = s["bytes"] / (s["total_ms"] * 1e-3) / 1e9
+        kernels[name] = ent
+    roofline = None
+    if "ns_gemm" in kstats:
+        s = kstats["ns_gemm"]
+        achieved = s["flops"] / (s["total_ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "ns_gemm_kernel<bf16>" if cfg.dtype == "bf16" else
+                    "ns_gemm_kernel<f32>", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak, "traffic": None,
+                    "per_launch_flops": s["flops"] / max(s["launches"], 1),
+                    "avg_launch_ms": s["total_ms"] / max(s["launches"], 1)}
+    ns_kernel_ms = sum(kstats[k]["total_ms"] for k in ("syrk", "ns_gemm") if k in kstats) / args.steps
+
+    out = {
+        "metric": "Muon step ms + NS TFLOP/s (% of MFMA peak), Llama-8B-shaped matrix set",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.key}: {cfg.count} matrices "
+                               f"({', '.join(sorted(set(f'{m.rows}x{m.cols}' for m in cfg.matrices)))}), "
+                               f"{cfg.dtype} grads/params, fp32 momentum, ns_steps={ns_steps}, "
+                               f"mu={cfg.momentum}, nesterov={cfg.nesterov}, lr={cfg.lr}",
+                   "matrices": cfg.count, "ns_steps": ns_steps, "parallelism": "single-gpu"},
+        "ns_tflops_kernels": (ns_total / (ns_kernel_ms * 1e-3) / 1e12) if ns_kernel_ms > 0 else None,
+        "pct_mfma_peak": 100.0 * value / peak,
+        "roofline": roofline,
+        "kernels": kernels,
+        "backend": nsa.backend_info(),
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        # one q_proj (4096x4096) and one k_proj (1024x4096) of layer 0
+        sample = [0, 1] if cfg.key == "llama3_8b" else [0]
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, sample, ns_steps, float(np.float32(cfg.momentum)), cfg.lr)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

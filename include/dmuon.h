@@ -1,0 +1,166 @@
+/*
+ * dmuon.h -- batched Muon optimizer step for AMD Instinct MI355X (gfx950).
+ *
+ * One call runs the Muon update over a whole set of 2-D weight matrices on one
+ * GPU stream:
+ *
+ *   buf <- mu * buf + grad                          momentum (fp32 state)
+ *   Y   <- grad + mu * buf   (Nesterov)  or  buf    Newton-Schulz input
+ *   U   <- NS_k(Y)                                  numel >= 100000
+ *   U   <- Y                                        numel <  100000
+ *   p   <- p - lr * lr_scale_i * U
+ *
+ * where NS_k normalises by the Frobenius norm (+1e-7), iterates on the wide
+ * orientation (the transpose when rows > cols) and applies k times the cubic
+ * map X <- 1.5 X - 0.5 (X X^T) X.
+ *
+ * Sources: DMuon blog post "DMuon：让矩阵正交化优化器达到接近 AdamW 的分布式训练开销",
+ * sections "Muon 核心：Newton-Schulz 迭代" (normalisation, cubic map, transpose
+ * to the wide side) and "代码实现" (VanillaMuon: momentum, non-matrix branch,
+ * update); DMuon training guide "训练指南", table "超参数指南" (lr, momentum,
+ * ns_steps, nesterov: ns_input = grad + mu * buf) and section "编写 Predicate"
+ * (numel < 100_000 is too small for NS).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Matrices are dense, row-major, contiguous: element (r, c) of matrix i is at
+ *   offset r * cols[i] + c.  rows[i], cols[i] >= 1 and <= DMUON_MAX_DIM.
+ * - Tensor pointers are device pointers; the pointer arrays themselves, the
+ *   shape arrays and lr_scale are host arrays, read only during the call.
+ * - All tensors and the workspace are owned by the caller.  The library
+ *   allocates no device memory; it keeps no state between calls other than
+ *   per-device capability checks and the optional profiler record.
+ * - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
+ *   and the call returns without synchronising.  Inputs must stay valid and
+ *   unmodified until the stream reaches the end of the enqueued work.
+ * - The workspace must hold at least the queried number of bytes and must not
+ *   be used by anything else until the enqueued work completes.  Two calls may
+ *   run concurrently only with distinct workspaces and disjoint outputs.
+ * - Argument errors are detected before anything is enqueued; nothing is
+ *   modified in that case.  A later DMUON_ERR_HIP means a launch failed and the
+ *   outputs are unspecified.
+ * - Results are bitwise reproducible for the same inputs, and a matrix's result
+ *   does not depend on the other matrices in the batch or their order.
+ */
+#ifndef DMUON_H
+#define DMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of gradients, parameters and Newton-Schulz operands.  The blog's
+ * newton_schulz accepts float32 or bfloat16.  Momentum is always float32. */
+#define DMUON_F32 0
+#define DMUON_BF16 1
+
+/* Status codes. */
+#define DMUON_OK 0
+#define DMUON_ERR_INVALID_ARG 1        /* bad count, shape, pointer, step count, ... */
+#define DMUON_ERR_UNSUPPORTED_DTYPE 2  /* dtype is neither DMUON_F32 nor DMUON_BF16 */
+#define DMUON_ERR_WORKSPACE 3          /* workspace NULL or smaller than the query */
+#define DMUON_ERR_NO_DEVICE 4          /* no HIP device visible */
+#define DMUON_ERR_UNSUPPORTED_ARCH 5   /* current device is not gfx950 */
+#define DMUON_ERR_HIP 6                /* a HIP runtime call or launch failed */
+
+/* Training guide, "编写 Predicate": matrices with numel < 100_000 skip NS. */
+#define DMUON_MIN_NS_NUMEL 100000
+/* Largest accepted rows or cols. */
+#define DMUON_MAX_DIM 65536
+/* Largest accepted ns_steps. */
+#define DMUON_MAX_NS_STEPS 64
+
+/*
+ * Workspace size for dmuon_ns_batched over the given shapes, in bytes.
+ * Writes *bytes_out and returns DMUON_OK, or an argument error.  Needs no GPU.
+ */
+int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                             size_t* bytes_out);
+
+/*
+ * Newton-Schulz orthogonalisation of `count` independent matrices
+ * (blog post, "Muon 核心：Newton-Schulz 迭代" and the newton_schulz listing of
+ * "代码实现"):
+ *
+ *   out_i = NS_{ns_steps}(x_i)
+ *
+ * x_in[i]  : device, rows[i] x cols[i], `dtype`, read only.
+ * x_out[i] : device, rows[i] x cols[i], `dtype`, written (RNE for bf16).  May
+ *            equal x_in[i]; must not overlap any other input or output.
+ * ns_steps : 0 .. DMUON_MAX_NS_STEPS; 0 returns the normalised input.
+ * Every matrix is orthogonalised, whatever its size.  bf16 inputs run the
+ * contractions on bf16 operands with fp32 accumulation and an fp32 iterate.
+ */
+int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out,
+                     const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
+                     void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Workspace size for dmuon_muon_step over the given shapes, in bytes.
+ * Needs no GPU.
+ */
+int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                                    size_t* bytes_out);
+
+/*
+ * One Muon step over `count` matrices (blog post VanillaMuon.step with the
+ * training guide's Nesterov input; equations at the top of this header).
+ *
+ * params[i]     : device, rows x cols, `dtype`; updated in place (RNE for bf16).
+ * grads[i]      : device, rows x cols, `dtype`; read only.
+ * momentum[i]   : device, rows x cols, float32; updated in place.  Start from
+ *                 zeros for a fresh optimizer.
+ * mu            : momentum coefficient (0.95 in the pages' defaults).
+ * nesterov      : nonzero -> Y = grad + mu * buf (with the updated buf).
+ * ns_steps      : 0 .. DMUON_MAX_NS_STEPS (5 in the pages' defaults).
+ * lr            : learning rate (0.02 in the pages' defaults).
+ * lr_scale      : host array of `count` floats multiplying lr per matrix, or
+ *                 NULL for 1.0 (the training guide names 0.2*sqrt(max(m,n))).
+ * update_out    : NULL, or a host array of `count` device pointers (entries
+ *                 may be NULL) receiving U_i as float32, rows x cols.
+ * norms_out     : NULL, or a device float32 array of `count` entries receiving
+ *                 ||Y_i||_F.
+ * params, grads, momentum and non-NULL update_out entries must be distinct
+ * non-overlapping buffers.
+ */
+int dmuon_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
+                    const int64_t* rows, const int64_t* cols, int dtype,
+                    int ns_steps, float mu, int nesterov, float lr, const float* lr_scale,
+                    float* const* update_out, float* norms_out,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Static text for a status code. */
+const char* dmuon_status_string(int status);
+
+/* Details of the last error returned on the calling thread ("" if none). */
+const char* dmuon_last_error(void);
+
+/* Build and kernel description, the analogue of the pages' get_ns_backend()
+ * string (training guide, "检查 NS 后端"). */
+const char* dmuon_backend_info(void);
+
+/*
+ * Kernel-level timing.  While enabled, every kernel the library enqueues is
+ * bracketed by a pair of HIP events on its stream.  dmuon_profile_read waits
+ * for those events, returns per-kernel totals and clears the record.
+ */
+typedef struct {
+    char name[40];      /* kernel family, e.g. "ns_gemm" */
+    int64_t launches;   /* launches recorded */
+    double total_ms;    /* sum of event-measured launch durations */
+    double flops;       /* algorithmic flops summed over those launches */
+    double bytes;       /* algorithmic HBM bytes summed over those launches */
+} dmuon_kernel_stat;
+
+int dmuon_profile_enable(int on);
+/* Fills up to `max_stats` entries and sets *n_stats; returns a status. */
+int dmuon_profile_read(dmuon_kernel_stat* stats, int max_stats, int* n_stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMUON_H */

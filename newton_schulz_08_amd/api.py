@@ -1,0 +1,193 @@
+"""Python binding of the dmuon C ABI: argument marshalling only.
+
+Tensors are torch CUDA (HIP) tensors used as plain device memory; every step of
+the Muon update runs in the HIP kernels of libdmuon.so.  Names mirror the C
+entry points in include/dmuon.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import check
+
+_DT = {torch.float32: _lib.DMUON_F32, torch.bfloat16: _lib.DMUON_BF16}
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    try:
+        return _DT[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dtype}; use torch.float32 or torch.bfloat16") from None
+
+
+def _shape_arrays(shapes):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(s[1]) for s in shapes])
+    return rows, cols
+
+
+def _ptrs(tensors) -> ctypes.Array:
+    n = len(tensors)
+    return (ctypes.c_void_p * max(n, 1))(*[None if t is None else t.data_ptr() for t in tensors])
+
+
+def _check_matrix(t: torch.Tensor, name: str, dtype: Optional[torch.dtype] = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != 2:
+        # blog post "常见错误" 2: Newton-Schulz is defined on matrices only
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def ns_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtype) -> int:
+    rows, cols = _shape_arrays(shapes)
+    out = ctypes.c_size_t(0)
+    check(_lib.load().dmuon_ns_workspace_bytes(len(shapes), rows, cols, dtype_code(dtype), ctypes.byref(out)),
+          "dmuon_ns_workspace_bytes")
+    return int(out.value)
+
+
+def muon_step_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtype) -> int:
+    rows, cols = _shape_arrays(shapes)
+    out = ctypes.c_size_t(0)
+    check(_lib.load().dmuon_muon_step_workspace_bytes(len(shapes), rows, cols, dtype_code(dtype),
+                                                      ctypes.byref(out)),
+          "dmuon_muon_step_workspace_bytes")
+    return int(out.value)
+
+
+def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A uint8 device buffer of at least nbytes, 256-byte aligned."""
+    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+    if ws.data_ptr() % 256:
+        raise RuntimeError("allocator returned a workspace that is not 256-byte aligned")
+    return ws
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def ns_batched(xs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]] = None, ns_steps: int = 5,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> List[torch.Tensor]:
+    """dmuon_ns_batched: out_i = NS_{ns_steps}(x_i) for every matrix."""
+    if len(xs) == 0:
+        return []
+    dt = xs[0].dtype
+    for i, x in enumerate(xs):
+        _check_matrix(x, f"xs[{i}]", dt)
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    for i, (o, x) in enumerate(zip(outs, xs)):
+        _check_matrix(o, f"outs[{i}]", dt)
+        if o.shape != x.shape:
+            raise ValueError(f"outs[{i}] shape {tuple(o.shape)} != {tuple(x.shape)}")
+    shapes = [tuple(x.shape) for x in xs]
+    need = ns_workspace_bytes(shapes, dt)
+    if workspace is None:
+        workspace = alloc_workspace(need, xs[0].device)
+    rows, cols = _shape_arrays(shapes)
+    check(_lib.load().dmuon_ns_batched(len(xs), _ptrs(xs), _ptrs(outs), rows, cols, dtype_code(dt), int(ns_steps),
+                                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                       ctypes.c_void_p(_stream_handle(stream))),
+          "dmuon_ns_batched")
+    return list(outs)
+
+
+class MuonStep:
+    """Pre-marshalled dmuon_muon_step over a fixed set of tensors.
+
+    Builds the pointer and shape arrays once, so repeated steps (a training
+    loop, the benchmark) pay only the C call.  The workspace is allocated here
+    unless given.
+    """
+
+    def __init__(self, params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                 momentum: Sequence[torch.Tensor], *, ns_steps: int = 5, mu: float = 0.95, nesterov: bool = True,
+                 lr: float = 0.02, lr_scale: Optional[Sequence[float]] = None,
+                 update_out: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                 norms_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+        n = len(params)
+        if not (len(grads) == len(momentum) == n):
+            raise ValueError("params, grads and momentum must have the same length")
+        if n == 0:
+            raise ValueError("empty parameter set")
+        dt = params[0].dtype
+        for i in range(n):
+            _check_matrix(params[i], f"params[{i}]", dt)
+            _check_matrix(grads[i], f"grads[{i}]", dt)
+            _check_matrix(momentum[i], f"momentum[{i}]", torch.float32)
+            if grads[i].shape != params[i].shape or momentum[i].shape != params[i].shape:
+                raise ValueError(f"matrix {i}: params/grads/momentum shapes differ")
+        if update_out is not None:
+            if len(update_out) != n:
+                raise ValueError("update_out must have one entry per matrix")
+            for i, u in enumerate(update_out):
+                if u is not None:
+                    _check_matrix(u, f"update_out[{i}]", torch.float32)
+                    if u.shape != params[i].shape:
+                        raise ValueError(f"update_out[{i}] has the wrong shape")
+        if norms_out is not None:
+            if norms_out.dtype != torch.float32 or not norms_out.is_cuda or norms_out.numel() < n:
+                raise ValueError("norms_out must be a float32 device tensor with one entry per matrix")
+        self.count = n
+        self.dtype = dt
+        self.shapes = [tuple(p.shape) for p in params]
+        self._keep = (list(params), list(grads), list(momentum), update_out, norms_out)
+        self._params = _ptrs(params)
+        self._grads = _ptrs(grads)
+        self._mom = _ptrs(momentum)
+        self._rows, self._cols = _shape_arrays(self.shapes)
+        self._upd = _ptrs(update_out) if update_out is not None else None
+        self._norms = ctypes.c_void_p(norms_out.data_ptr()) if norms_out is not None else None
+        self._scale = (ctypes.c_float * n)(*[float(s) for s in lr_scale]) if lr_scale is not None else None
+        self.ns_steps, self.mu, self.nesterov, self.lr = int(ns_steps), float(mu), bool(nesterov), float(lr)
+        self.workspace_bytes = muon_step_workspace_bytes(self.shapes, dt)
+        self.workspace = workspace if workspace is not None else alloc_workspace(self.workspace_bytes,
+                                                                                 params[0].device)
+        if self.workspace.numel() < self.workspace_bytes:
+            raise ValueError("workspace too small")
+        self._lib = _lib.load()
+
+    def __call__(self, stream=None) -> None:
+        check(self._lib.dmuon_muon_step(
+            self.count, self._params, self._grads, self._mom, self._rows, self._cols, dtype_code(self.dtype),
+            self.ns_steps, ctypes.c_float(self.mu), 1 if self.nesterov else 0, ctypes.c_float(self.lr),
+            self._scale, self._upd, self._norms, ctypes.c_void_p(self.workspace.data_ptr()),
+            self.workspace.numel(), ctypes.c_void_p(_stream_handle(stream))), "dmuon_muon_step")
+
+
+def muon_step(params, grads, momentum, **kw) -> None:
+    """dmuon_muon_step over lists of tensors (one-shot form of MuonStep)."""
+    stream = kw.pop("stream", None)
+    MuonStep(params, grads, momentum, **kw)(stream)
+
+
+def backend_info() -> str:
+    return _lib.load().dmuon_backend_info().decode()
+
+
+def profile_enable(on: bool = True) -> None:
+    check(_lib.load().dmuon_profile_enable(1 if on else 0), "dmuon_profile_enable")
+
+
+def profile_read() -> dict:
+    """{kernel family: {launches, total_ms, flops, bytes}} since the last read."""
+    stats = (_lib.KernelStat * 16)()
+    n = ctypes.c_int(0)
+    check(_lib.load().dmuon_profile_read(stats, 16, ctypes.byref(n)), "dmuon_profile_read")
+    return {stats[i].name.decode(): dict(launches=stats[i].launches, total_ms=stats[i].total_ms,
+                                         flops=stats[i].flops, bytes=stats[i].bytes) for i in range(n.value)}

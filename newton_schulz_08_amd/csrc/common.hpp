@@ -1,0 +1,80 @@
+// Shared definitions between the host planner and the gfx950 kernels.
+//
+// Data layout in HBM (per Newton-Schulz matrix, "wide" orientation: m' rows =
+// min(rows, cols), n' cols = max(rows, cols); both padded up to multiples of
+// kTile so the contraction kernels run without bounds checks):
+//
+//   xm  float32  Mp x Np  row-major   iterate (fp32 master copy)
+//   xs  dtype    Mp x Np  row-major   operand of the Gram product (aliases xm for fp32)
+//   xt  dtype    Np x Mp  row-major   transposed iterate, operand of A*X (two, ping-pong)
+//   a   dtype    Mp x Mp  row-major   Gram matrix X X^T (symmetric)
+//
+// Padding rows/cols hold zeros, which every stage preserves.
+#pragma once
+
+#include <stdint.h>
+
+namespace dmuon {
+
+constexpr int kTile = 256;           // MFMA block tile (rows and cols)
+constexpr int kEwTile = 64;          // elementwise / transpose tile
+constexpr int kEwThreads = 256;
+constexpr float kNormEps = 1e-7f;    // blog post: G / (G.norm() + 1e-7)
+
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+// Prologue modes.
+enum PrologueMode : int {
+  kModeMuon = 0,   // momentum + Nesterov + route
+  kModeNsOnly = 1, // Y = x (dmuon_ns_batched)
+};
+
+// One matrix of the call.  Lives in the workspace; 128 bytes.
+struct alignas(16) MatDesc {
+  const void* g;     // grad (muon step) or x_in (ns only)
+  float* buf;        // momentum buffer (muon step) or nullptr
+  void* p;           // params (muon step) or x_out (ns only)
+  float* upd;        // optional fp32 update output (original orientation)
+  float* xm;         // workspace: fp32 iterate, Mp x Np
+  void* xs;          // workspace: Gram operand, Mp x Np (== xm for fp32)
+  void* xt0;         // workspace: transposed iterate, Np x Mp (even steps)
+  void* xt1;         // workspace: transposed iterate, Np x Mp (odd steps)
+  void* a;           // workspace: Gram matrix, Mp x Mp
+  int m, n;          // caller shape (rows, cols)
+  int mp, np;        // padded wide dims (NS route only)
+  int tr;            // 1 when rows > cols (iterate on the transpose)
+  int ns;            // 1 = Newton-Schulz route, 0 = elementwise route
+  int out_index;     // position in the caller's arrays (norms_out)
+  int ew_tile0;      // first prologue tile of this matrix
+  int ew_tiles_c;    // prologue tiles along the covered column extent
+  int ew_rows;       // covered extent (rows) for the prologue
+  int ew_cols;       // covered extent (cols) for the prologue
+  int vec_ok;        // 1 when 4-element vector access is aligned for g/buf/p/upd
+  float lr_scale;
+  float pad_[3];
+};
+static_assert(sizeof(MatDesc) % 16 == 0, "MatDesc layout");
+
+// A run of equally shaped Newton-Schulz matrices inside one contraction launch.
+struct alignas(16) Segment {
+  int tile0;          // first logical tile of the segment
+  int ntiles;         // count * tiles_per_mat
+  int tiles_per_mat;
+  int mat0;           // first entry in the NS descriptor list
+  int tm, tn;         // tile grid: rows, cols of 256-tiles (SYRK: tm == tn)
+  int kdim;           // contraction length in elements
+  int pad_;
+};
+static_assert(sizeof(Segment) == 32, "Segment layout");
+
+// Per-matrix scalars produced by the norm reduction.
+struct alignas(16) MatScale {
+  float c;      // 1 / (||Y|| + eps)
+  float c2;     // c * c
+  float norm;   // ||Y||
+  float pad_;
+};
+
+constexpr int kMaxSegments = 64;
+
+}  // namespace dmuon

@@ -1,0 +1,617 @@
+// C-ABI entry points: argument validation, the ragged-batch planner and the
+// launch sequence of one Muon step on a caller stream.
+//
+// Planner ("scheduler"): every matrix is routed (numel < 100000 -> elementwise
+// route, training guide "编写 Predicate"), oriented (rows > cols -> iterate on
+// the transpose, blog "代码实现"), and Newton-Schulz matrices are grouped by
+// padded wide shape.  Each group becomes one segment of the contraction
+// launches, so a whole set of differently shaped projections runs as
+// 2 launches per Newton-Schulz step, plus a prologue and a norm reduction.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/dmuon.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dmuon {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+struct MatPlan {
+  int index;          // caller index
+  int64_t m, n;
+  bool ns, tr;
+  int64_t mp, np;     // padded wide dims
+  int ew_rows, ew_cols, ew_tiles;
+  size_t off_xm, off_xs, off_xt0, off_xt1, off_a;
+};
+
+struct Group {
+  int64_t mp, np;
+  int first, count;   // range in the NS part of the descriptor order
+};
+
+struct Plan {
+  int dt = kF32;
+  int count = 0;
+  std::vector<MatPlan> mats;   // descriptor order: NS groups first, then elementwise
+  std::vector<Group> groups;
+  int n_ns = 0;
+  int total_tiles = 0;
+  size_t off_descs = 0, off_prefix = 0, off_partials = 0, off_scales = 0;
+  size_t total = 0;
+  double syrk_flops = 0.0, gemm_flops = 0.0;
+};
+
+size_t elem_bytes(int dt) { return dt == kBF16 ? 2 : 4; }
+
+int validate_shapes(int count, const int64_t* rows, const int64_t* cols, int dt) {
+  if (count < 0) return fail(DMUON_ERR_INVALID_ARG, "count < 0");
+  if (dt != kF32 && dt != kBF16) return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "dtype must be DMUON_F32 or DMUON_BF16");
+  if (count == 0) return DMUON_OK;
+  if (!rows || !cols) return fail(DMUON_ERR_INVALID_ARG, "rows/cols array is NULL");
+  for (int i = 0; i < count; ++i) {
+    if (rows[i] < 1 || cols[i] < 1 || rows[i] > DMUON_MAX_DIM || cols[i] > DMUON_MAX_DIM)
+      return fail(DMUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": shape " + std::to_string(rows[i]) + "x" +
+                                             std::to_string(cols[i]) + " outside [1, DMUON_MAX_DIM]");
+  }
+  return DMUON_OK;
+}
+
+// Build the plan.  `route` = apply the numel < 100000 elementwise route.
+Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool route) {
+  Plan pl;
+  pl.dt = dt;
+  pl.count = count;
+  std::vector<MatPlan> ns_mats, ew_mats;
+  for (int i = 0; i < count; ++i) {
+    MatPlan mp{};
+    mp.index = i;
+    mp.m = rows[i];
+    mp.n = cols[i];
+    mp.ns = !route || (mp.m * mp.n >= DMUON_MIN_NS_NUMEL);
+    mp.tr = mp.m > mp.n;
+    if (mp.ns) {
+      mp.mp = round_up(std::min(mp.m, mp.n), kTile);
+      mp.np = round_up(std::max(mp.m, mp.n), kTile);
+      // prologue covers the padded extent in the caller's orientation
+      mp.ew_rows = static_cast<int>(mp.tr ? mp.np : mp.mp);
+      mp.ew_cols = static_cast<int>(mp.tr ? mp.mp : mp.np);
+      ns_mats.push_back(mp);
+    } else {
+      mp.ew_rows = static_cast<int>(round_up(mp.m, kEwTile));
+      mp.ew_cols = static_cast<int>(round_up(mp.n, kEwTile));
+      ew_mats.push_back(mp);
+    }
+  }
+  // group NS matrices by padded wide shape; largest contraction first
+  std::stable_sort(ns_mats.begin(), ns_mats.end(), [](const MatPlan& a, const MatPlan& b) {
+    const double ca = static_cast<double>(a.mp) * a.mp * a.np, cb = static_cast<double>(b.mp) * b.mp * b.np;
+    if (ca != cb) return ca > cb;
+    return std::make_tuple(a.mp, a.np) < std::make_tuple(b.mp, b.np);
+  });
+  for (size_t k = 0; k < ns_mats.size(); ++k) {
+    if (pl.groups.empty() || pl.groups.back().mp != ns_mats[k].mp || pl.groups.back().np != ns_mats[k].np)
+      pl.groups.push_back(Group{ns_mats[k].mp, ns_mats[k].np, static_cast<int>(k), 0});
+    pl.groups.back().count++;
+  }
+  pl.n_ns = static_cast<int>(ns_mats.size());
+  pl.mats = ns_mats;
+  pl.mats.insert(pl.mats.end(), ew_mats.begin(), ew_mats.end());
+
+  int tiles = 0;
+  for (auto& mp : pl.mats) {
+    mp.ew_tiles = (mp.ew_rows / kEwTile) * (mp.ew_cols / kEwTile);
+    tiles += mp.ew_tiles;
+  }
+  pl.total_tiles = tiles;
+
+  size_t off = 0;
+  pl.off_descs = off;
+  off = align_up(off + sizeof(MatDesc) * count);
+  pl.off_prefix = off;
+  off = align_up(off + sizeof(int) * (count + 1));
+  pl.off_partials = off;
+  off = align_up(off + sizeof(float) * std::max(tiles, 1));
+  pl.off_scales = off;
+  off = align_up(off + sizeof(MatScale) * count);
+  const size_t eb = elem_bytes(dt);
+  for (int k = 0; k < pl.n_ns; ++k) {
+    MatPlan& mp = pl.mats[k];
+    const size_t wide = static_cast<size_t>(mp.mp) * mp.np;
+    mp.off_xm = off;
+    off = align_up(off + 4 * wide);
+    if (dt == kBF16) {
+      mp.off_xs = off;
+      off = align_up(off + eb * wide);
+    } else {
+      mp.off_xs = mp.off_xm;
+    }
+    mp.off_xt0 = off;
+    off = align_up(off + eb * wide);
+    mp.off_xt1 = off;
+    off = align_up(off + eb * wide);
+    mp.off_a = off;
+    off = align_up(off + eb * static_cast<size_t>(mp.mp) * mp.mp);
+    const double mm = static_cast<double>(std::min(mp.m, mp.n)), nn = static_cast<double>(std::max(mp.m, mp.n));
+    pl.syrk_flops += mm * (mm + 1.0) * nn;
+    pl.gemm_flops += 2.0 * mm * mm * nn + 3.0 * mm * nn;
+  }
+  pl.total = std::max<size_t>(off, kAlign);
+  return pl;
+}
+
+// ---------------------------------------------------------------- device checks
+std::mutex g_dev_mu;
+std::map<int, int> g_dev_status;  // device -> status
+
+int check_device() {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return fail(DMUON_ERR_NO_DEVICE, "no HIP device visible");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DMUON_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev_status.find(dev);
+  if (it != g_dev_status.end()) {
+    if (it->second != DMUON_OK) return fail(it->second, "current device is not gfx950");
+    return DMUON_OK;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(DMUON_ERR_HIP, "hipGetDeviceProperties failed");
+  const int st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? DMUON_OK : DMUON_ERR_UNSUPPORTED_ARCH;
+  g_dev_status[dev] = st;
+  if (st != DMUON_OK) return fail(st, std::string("current device is ") + prop.gcnArchName + ", not gfx950");
+  return DMUON_OK;
+}
+
+// ---------------------------------------------------------------- profiler
+enum KernelClass { kKPrologue = 0, kKNorm, kKSyrk, kKGemm, kKApply, kKNumClasses };
+const char* kClassNames[kKNumClasses] = {"prologue", "norm_finalize", "syrk", "ns_gemm", "apply_x0"};
+
+struct ProfRecord {
+  int cls;
+  hipEvent_t start, stop;
+  double flops, bytes;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` on `stream`, bracketed by events when profiling is on.
+template <typename F>
+hipError_t timed(int cls, double flops, double bytes, hipStream_t stream, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    on = g_prof_on;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    a = take_event();
+    b = take_event();
+  }
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, stream);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, stream);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_records.push_back(ProfRecord{cls, a, b, flops, bytes});
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- execution
+struct Call {
+  int mode;
+  const void* const* in;     // grads or x_in
+  float* const* buf;         // momentum (muon)
+  void* const* out;          // params or x_out
+  float* const* upd;         // update_out (muon, nullable)
+  const float* lr_scale;
+  float* norms_out;
+  int ns_steps;
+  float mu, lr;
+  int nesterov;
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const int dt = pl.dt;
+  const size_t eb = elem_bytes(dt);
+
+  std::vector<MatDesc> descs(pl.count);
+  std::vector<int> prefix(pl.count + 1);
+  int tile0 = 0;
+  for (int k = 0; k < pl.count; ++k) {
+    const MatPlan& mp = pl.mats[k];
+    MatDesc& d = descs[k];
+    std::memset(&d, 0, sizeof(d));
+    const int i = mp.index;
+    d.g = call.in[i];
+    d.buf = call.buf ? call.buf[i] : nullptr;
+    d.p = call.out[i];
+    d.upd = call.upd ? call.upd[i] : nullptr;
+    if (mp.ns) {
+      d.xm = reinterpret_cast<float*>(ws + mp.off_xm);
+      d.xs = ws + mp.off_xs;
+      d.xt0 = ws + mp.off_xt0;
+      d.xt1 = ws + mp.off_xt1;
+      d.a = ws + mp.off_a;
+      d.mp = static_cast<int>(mp.mp);
+      d.np = static_cast<int>(mp.np);
+    }
+    d.m = static_cast<int>(mp.m);
+    d.n = static_cast<int>(mp.n);
+    d.tr = mp.tr ? 1 : 0;
+    d.ns = mp.ns ? 1 : 0;
+    d.out_index = i;
+    d.ew_tile0 = tile0;
+    d.ew_tiles_c = mp.ew_cols / kEwTile;
+    d.ew_rows = mp.ew_rows;
+    d.ew_cols = mp.ew_cols;
+    const size_t va = 4 * eb;  // 4 elements of dtype
+    bool vec = (mp.n % 4) == 0 && aligned(d.g, va) && aligned(d.p, va);
+    if (d.buf) vec = vec && aligned(d.buf, 16);
+    if (d.upd) vec = vec && aligned(d.upd, 16);
+    d.vec_ok = vec ? 1 : 0;
+    d.lr_scale = call.lr_scale ? call.lr_scale[i] : 1.0f;
+    prefix[k] = tile0;
+    tile0 += mp.ew_tiles;
+  }
+  prefix[pl.count] = tile0;
+
+  MatDesc* d_descs = reinterpret_cast<MatDesc*>(ws + pl.off_descs);
+  int* d_prefix = reinterpret_cast<int*>(ws + pl.off_prefix);
+  float* d_partials = reinterpret_cast<float*>(ws + pl.off_partials);
+  MatScale* d_scales = reinterpret_cast<MatScale*>(ws + pl.off_scales);
+
+  // Pageable-source copies: the runtime has consumed the host data when the
+  // call returns, so the vectors may go out of scope afterwards.
+  if (hipMemcpyAsync(d_descs, descs.data(), sizeof(MatDesc) * pl.count, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(d_prefix, prefix.data(), sizeof(int) * (pl.count + 1), hipMemcpyHostToDevice, stream) !=
+          hipSuccess)
+    return fail(DMUON_ERR_HIP, std::string("descriptor upload failed: ") + hipGetErrorString(hipGetLastError()));
+
+  // algorithmic bytes of the prologue: read g, read+write momentum (muon) and,
+  // for the elementwise route, read+write p
+  double pro_bytes = 0.0;
+  for (const auto& mp : pl.mats) {
+    const double ne = static_cast<double>(mp.m) * mp.n;
+    double b = eb * ne;
+    if (call.mode == kModeMuon) b += 8.0 * ne + (mp.ns ? 0.0 : 2.0 * eb * ne);
+    pro_bytes += b;
+  }
+
+  const int ew_grid = std::min(pl.total_tiles, 256 * 8);
+  hipError_t e = timed(kKPrologue, 0.0, pro_bytes, stream, [&] {
+    return launch_prologue(dt, d_descs, d_prefix, pl.count, pl.total_tiles, d_partials, call.mode, call.mu,
+                           call.nesterov, call.lr, ew_grid, stream);
+  });
+  if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
+  e = timed(kKNorm, 0.0, 4.0 * pl.total_tiles, stream, [&] {
+    return launch_norm_finalize(d_descs, d_prefix, pl.count, d_partials, d_scales, call.norms_out, stream);
+  });
+  if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("norm launch: ") + hipGetErrorString(e));
+  if (pl.n_ns == 0) return DMUON_OK;
+
+  if (call.ns_steps == 0) {
+    e = timed(kKApply, 0.0, 0.0, stream, [&] {
+      return launch_apply_x0(dt, d_descs, d_prefix, pl.count, pl.total_tiles, d_scales, call.mode, call.lr, ew_grid,
+                             stream);
+    });
+    if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("apply launch: ") + hipGetErrorString(e));
+    return DMUON_OK;
+  }
+
+  // contraction launches: one segment per shape group, longest K first
+  struct SegSpec {
+    Segment s;
+    double flops;
+  };
+  std::vector<SegSpec> syrk_segs, gemm_segs;
+  for (const Group& g : pl.groups) {
+    const int T = static_cast<int>(g.mp / kTile), TN = static_cast<int>(g.np / kTile);
+    double sf = 0.0, gf = 0.0;
+    for (int k = g.first; k < g.first + g.count; ++k) {
+      const double mm = static_cast<double>(std::min(pl.mats[k].m, pl.mats[k].n));
+      const double nn = static_cast<double>(std::max(pl.mats[k].m, pl.mats[k].n));
+      sf += mm * (mm + 1.0) * nn;
+      gf += 2.0 * mm * mm * nn + 3.0 * mm * nn;
+    }
+    Segment s{};
+    s.mat0 = g.first;
+    s.tiles_per_mat = T * (T + 1) / 2;
+    s.ntiles = s.tiles_per_mat * g.count;
+    s.tm = T;
+    s.tn = T;
+    s.kdim = static_cast<int>(g.np);
+    syrk_segs.push_back(SegSpec{s, sf});
+    Segment q{};
+    q.mat0 = g.first;
+    q.tiles_per_mat = T * TN;
+    q.ntiles = q.tiles_per_mat * g.count;
+    q.tm = T;
+    q.tn = TN;
+    q.kdim = static_cast<int>(g.mp);
+    gemm_segs.push_back(SegSpec{q, gf});
+  }
+  auto by_k = [](const SegSpec& a, const SegSpec& b) { return a.s.kdim > b.s.kdim; };
+  std::stable_sort(syrk_segs.begin(), syrk_segs.end(), by_k);
+  std::stable_sort(gemm_segs.begin(), gemm_segs.end(), by_k);
+
+  auto batches = [](const std::vector<SegSpec>& segs) {
+    std::vector<std::pair<SegTable, std::pair<int, double>>> out;
+    for (size_t s0 = 0; s0 < segs.size(); s0 += kMaxSegPerLaunch) {
+      SegTable st{};
+      int tiles = 0;
+      double fl = 0.0;
+      for (size_t k = s0; k < std::min(segs.size(), s0 + kMaxSegPerLaunch); ++k) {
+        Segment s = segs[k].s;
+        s.tile0 = tiles;
+        tiles += s.ntiles;
+        fl += segs[k].flops;
+        st.seg[st.nseg++] = s;
+      }
+      out.push_back({st, {tiles, fl}});
+    }
+    return out;
+  };
+  const auto syrk_launches = batches(syrk_segs);
+  const auto gemm_launches = batches(gemm_segs);
+
+  for (int step = 0; step < call.ns_steps; ++step) {
+    for (const auto& L : syrk_launches) {
+      e = timed(kKSyrk, L.second.second, 0.0, stream, [&] {
+        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step == 0 ? 1 : 0, stream);
+      });
+      if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk launch: ") + hipGetErrorString(e));
+    }
+    const int last = (step + 1 == call.ns_steps) ? 1 : 0;
+    for (const auto& L : gemm_launches) {
+      e = timed(kKGemm, L.second.second, 0.0, stream, [&] {
+        return launch_ns_gemm(dt, d_descs, L.first, L.second.first, d_scales, step, last, call.mode, call.lr, stream);
+      });
+      if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("ns_gemm launch: ") + hipGetErrorString(e));
+    }
+  }
+  return DMUON_OK;
+}
+
+int check_ptr_array(int count, const void* const* a, const char* what, bool allow_null_entries) {
+  if (!a) return fail(DMUON_ERR_INVALID_ARG, std::string(what) + " array is NULL");
+  for (int i = 0; i < count; ++i)
+    if (!a[i] && !allow_null_entries)
+      return fail(DMUON_ERR_INVALID_ARG, std::string(what) + "[" + std::to_string(i) + "] is NULL");
+  return DMUON_OK;
+}
+
+// Distinct pointers among the given writable arrays (exact duplicates only).
+int check_distinct(const std::vector<std::pair<const void*, std::string>>& ptrs) {
+  std::vector<std::pair<const void*, std::string>> v;
+  for (const auto& p : ptrs)
+    if (p.first) v.push_back(p);
+  std::sort(v.begin(), v.end(), [](const auto& a, const auto& b) { return a.first < b.first; });
+  for (size_t k = 1; k < v.size(); ++k)
+    if (v[k].first == v[k - 1].first)
+      return fail(DMUON_ERR_INVALID_ARG, "buffers " + v[k - 1].second + " and " + v[k].second + " alias");
+  return DMUON_OK;
+}
+
+int ws_check(const Plan& pl, void* workspace, size_t bytes) {
+  if (!workspace) return fail(DMUON_ERR_WORKSPACE, "workspace is NULL");
+  if (bytes < pl.total)
+    return fail(DMUON_ERR_WORKSPACE, "workspace has " + std::to_string(bytes) + " bytes, needs " +
+                                         std::to_string(pl.total));
+  if (!aligned(workspace, kAlign)) return fail(DMUON_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return DMUON_OK;
+}
+
+}  // namespace
+}  // namespace dmuon
+
+using namespace dmuon;
+
+extern "C" {
+
+int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype, size_t* bytes_out) {
+  g_last_error.clear();
+  if (!bytes_out) return fail(DMUON_ERR_INVALID_ARG, "bytes_out is NULL");
+  int st = validate_shapes(count, rows, cols, dtype);
+  if (st != DMUON_OK) return st;
+  *bytes_out = count == 0 ? 0 : make_plan(count, rows, cols, dtype, false).total;
+  return DMUON_OK;
+}
+
+int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                                    size_t* bytes_out) {
+  g_last_error.clear();
+  if (!bytes_out) return fail(DMUON_ERR_INVALID_ARG, "bytes_out is NULL");
+  int st = validate_shapes(count, rows, cols, dtype);
+  if (st != DMUON_OK) return st;
+  *bytes_out = count == 0 ? 0 : make_plan(count, rows, cols, dtype, true).total;
+  return DMUON_OK;
+}
+
+int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out, const int64_t* rows,
+                     const int64_t* cols, int dtype, int ns_steps, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+  g_last_error.clear();
+  int st = validate_shapes(count, rows, cols, dtype);
+  if (st != DMUON_OK) return st;
+  if (ns_steps < 0 || ns_steps > DMUON_MAX_NS_STEPS)
+    return fail(DMUON_ERR_INVALID_ARG, "ns_steps outside [0, DMUON_MAX_NS_STEPS]");
+  if (count == 0) return DMUON_OK;
+  if ((st = check_ptr_array(count, x_in, "x_in", false)) != DMUON_OK) return st;
+  if ((st = check_ptr_array(count, reinterpret_cast<const void* const*>(x_out), "x_out", false)) != DMUON_OK)
+    return st;
+  std::vector<std::pair<const void*, std::string>> outs;
+  for (int i = 0; i < count; ++i) outs.push_back({x_out[i], "x_out[" + std::to_string(i) + "]"});
+  if ((st = check_distinct(outs)) != DMUON_OK) return st;
+  const Plan pl = make_plan(count, rows, cols, dtype, false);
+  if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
+  if ((st = check_device()) != DMUON_OK) return st;
+  Call call{};
+  call.mode = kModeNsOnly;
+  call.in = x_in;
+  call.out = x_out;
+  call.ns_steps = ns_steps;
+  return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+int dmuon_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
+                    const int64_t* rows, const int64_t* cols, int dtype, int ns_steps, float mu, int nesterov,
+                    float lr, const float* lr_scale, float* const* update_out, float* norms_out, void* workspace,
+                    size_t workspace_bytes, void* hip_stream) {
+  g_last_error.clear();
+  int st = validate_shapes(count, rows, cols, dtype);
+  if (st != DMUON_OK) return st;
+  if (ns_steps < 0 || ns_steps > DMUON_MAX_NS_STEPS)
+    return fail(DMUON_ERR_INVALID_ARG, "ns_steps outside [0, DMUON_MAX_NS_STEPS]");
+  if (!std::isfinite(mu) || !std::isfinite(lr)) return fail(DMUON_ERR_INVALID_ARG, "mu and lr must be finite");
+  if (count == 0) return DMUON_OK;
+  if ((st = check_ptr_array(count, reinterpret_cast<const void* const*>(params), "params", false)) != DMUON_OK)
+    return st;
+  if ((st = check_ptr_array(count, grads, "grads", false)) != DMUON_OK) return st;
+  if ((st = check_ptr_array(count, reinterpret_cast<const void* const*>(momentum), "momentum", false)) != DMUON_OK)
+    return st;
+  if (lr_scale)
+    for (int i = 0; i < count; ++i)
+      if (!std::isfinite(lr_scale[i])) return fail(DMUON_ERR_INVALID_ARG, "lr_scale entries must be finite");
+  std::vector<std::pair<const void*, std::string>> ptrs;
+  for (int i = 0; i < count; ++i) {
+    const std::string s = "[" + std::to_string(i) + "]";
+    ptrs.push_back({params[i], "params" + s});
+    ptrs.push_back({grads[i], "grads" + s});
+    ptrs.push_back({momentum[i], "momentum" + s});
+    if (update_out) ptrs.push_back({update_out[i], "update_out" + s});
+  }
+  if ((st = check_distinct(ptrs)) != DMUON_OK) return st;
+  const Plan pl = make_plan(count, rows, cols, dtype, true);
+  if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
+  if ((st = check_device()) != DMUON_OK) return st;
+  Call call{};
+  call.mode = kModeMuon;
+  call.in = grads;
+  call.buf = momentum;
+  call.out = params;
+  call.upd = update_out;
+  call.lr_scale = lr_scale;
+  call.norms_out = norms_out;
+  call.ns_steps = ns_steps;
+  call.mu = mu;
+  call.lr = lr;
+  call.nesterov = nesterov ? 1 : 0;
+  return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+const char* dmuon_status_string(int status) {
+  switch (status) {
+    case DMUON_OK: return "ok";
+    case DMUON_ERR_INVALID_ARG: return "invalid argument";
+    case DMUON_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case DMUON_ERR_WORKSPACE: return "workspace missing or too small";
+    case DMUON_ERR_NO_DEVICE: return "no HIP device";
+    case DMUON_ERR_UNSUPPORTED_ARCH: return "device is not gfx950";
+    case DMUON_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dmuon_last_error(void) { return g_last_error.c_str(); }
+
+const char* dmuon_backend_info(void) {
+  return "dmuon gfx950 | prologue: fused momentum/Nesterov/Frobenius partials, 64x64 LDS-transpose tiles"
+         " | syrk: lower-triangle 256x256 tiles + transposed mirror, v_mfma_f32_32x32x16_bf16 / 32x32x2_f32"
+         " | ns_gemm: 256x256 tiles, fused 1.5X-0.5AX epilogue, last step writes p -= lr*s*U"
+         " | ragged batch: shape-grouped segments, XCD-contiguous tile order | built " __DATE__;
+}
+
+int dmuon_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return DMUON_OK;
+}
+
+int dmuon_profile_read(dmuon_kernel_stat* stats, int max_stats, int* n_stats) {
+  g_last_error.clear();
+  if (!n_stats || (max_stats > 0 && !stats)) return fail(DMUON_ERR_INVALID_ARG, "NULL output");
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof_records);
+  }
+  dmuon_kernel_stat agg[kKNumClasses];
+  std::memset(agg, 0, sizeof(agg));
+  int status = DMUON_OK;
+  for (const auto& r : recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      status = fail(DMUON_ERR_HIP, "event timing failed");
+    agg[r.cls].launches++;
+    agg[r.cls].total_ms += ms;
+    agg[r.cls].flops += r.flops;
+    agg[r.cls].bytes += r.bytes;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (const auto& r : recs) {
+      g_event_pool.push_back(r.start);
+      g_event_pool.push_back(r.stop);
+    }
+  }
+  int n = 0;
+  for (int c = 0; c < kKNumClasses; ++c) {
+    if (agg[c].launches == 0) continue;
+    if (n < max_stats) {
+      stats[n] = agg[c];
+      std::snprintf(stats[n].name, sizeof(stats[n].name), "%s", kClassNames[c]);
+    }
+    ++n;
+  }
+  *n_stats = std::min(n, std::max(max_stats, 0));
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,313 @@
+// HBM-bound kernels of the Muon step on gfx950.
+//
+// prologue_kernel  -- one pass over every matrix, 64x64 tiles, 256 threads:
+//     buf <- mu * buf + g                       (blog post VanillaMuon: mul_ then add_)
+//     Y   <- g + mu * buf  or  buf              (training guide: nesterov ns_input)
+//     partial sum of Y^2 per tile               (Frobenius norm of the NS input)
+//   small matrices (numel < 100000, training guide "编写 Predicate"):
+//     p <- p - lr * s * Y, update_out <- Y      (blog VanillaMuon non-matrix branch)
+//   Newton-Schulz matrices: Y is written, unnormalised, as the fp32 iterate, its
+//   operand copy and its transpose in the wide orientation (the transposed
+//   stores go through an LDS tile so both sides stay coalesced).  The 1/||Y||
+//   scale is folded into the first Newton-Schulz step instead of a second pass.
+// norm_finalize_kernel -- fixed-order sum of each matrix's tile partials.
+// apply_x0_kernel -- ns_steps == 0 only: U = Y / (||Y|| + eps) to the caller.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dmuon {
+namespace {
+
+template <int DT> struct Elem;
+template <> struct Elem<kBF16> { using T = __bf16; };
+template <> struct Elem<kF32> { using T = float; };
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(__bf16 v) { return static_cast<float>(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* __restrict__ src, bool vec, int valid, float (&v)[4]) {
+  if (vec) {
+    if constexpr (sizeof(T) == 2) {
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(src);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = to_f32(x[e]);
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(src);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (e < valid) ? to_f32(src[e]) : 0.0f;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* __restrict__ dst, bool vec, int valid, const float (&v)[4]) {
+  if (vec) {
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(v[e]);
+      *reinterpret_cast<bf16x4*>(dst) = x;
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < valid) dst[e] = from_f32<T>(v[e]);
+  }
+}
+
+__device__ __forceinline__ int find_matrix(const int* __restrict__ prefix, int nmat, int t) {
+  int lo = 0, hi = nmat - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __restrict__ descs,
+                                                              const int* __restrict__ prefix, int nmat,
+                                                              int total_tiles, float* __restrict__ partials,
+                                                              int mode, float mu, int nesterov, float lr) {
+  using T = typename Elem<DT>::T;
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  __shared__ float red[kEwThreads / 64];
+  const int tid = threadIdx.x;
+  const int cl = (tid & 15) * 4;  // 4 consecutive columns
+  const int rl0 = tid >> 4;       // rows rl0 + 16 * pass
+
+  for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+    const MatDesc& d = descs[find_matrix(prefix, nmat, t)];
+    const int local = t - d.ew_tile0;
+    const int tr_ = local / d.ew_tiles_c;
+    const int r0 = tr_ * kEwTile, c0 = (local - tr_ * d.ew_tiles_c) * kEwTile;
+    const int m = d.m, n = d.n;
+    const bool ns = d.ns != 0, trn = d.tr != 0;
+    const int mp = d.mp, np = d.np;
+    const float step_lr = -lr * d.lr_scale;
+    float ss = 0.0f;
+
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rl = rl0 + 16 * pass;
+      const int r = r0 + rl, c = c0 + cl;
+      float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (r < m && c < n) {
+        const int valid = min(4, n - c);
+        const bool vec = d.vec_ok && valid == 4;
+        const long o = static_cast<long>(r) * n + c;
+        float g[4];
+        load4(static_cast<const T*>(d.g) + o, vec, valid, g);
+        if (mode == kModeMuon) {
+          float b[4];
+          load4(d.buf + o, vec, valid, b);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            b[e] = fmaf(mu, b[e], g[e]);
+            y[e] = nesterov ? fmaf(mu, b[e], g[e]) : b[e];
+          }
+          store4(d.buf + o, vec, valid, b);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = g[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e >= valid) y[e] = 0.0f;
+        if (!ns) {
+          float pv[4];
+          T* p = static_cast<T*>(d.p) + o;
+          load4(p, vec, valid, pv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = fmaf(step_lr, y[e], pv[e]);
+          store4(p, vec, valid, pv);
+          if (d.upd) store4(d.upd + o, vec, valid, y);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(y[e], y[e], ss);
+      if (ns) {
+        // the covered extent is padded to 256, so every tile position exists
+        if (!trn) {
+          const long w = static_cast<long>(r) * np + c;
+          store4(d.xm + w, true, 4, y);
+          if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs) + w, true, 4, y);
+        } else {
+          store4(static_cast<T*>(d.xt0) + static_cast<long>(r) * mp + c, true, 4, y);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[rl][cl + e] = y[e];
+      }
+    }
+
+    if (ns) {
+      __syncthreads();
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int j = rl0 + 16 * pass;  // input column -> output row
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = tile[cl + e][j];
+        if (!trn) {
+          store4(static_cast<T*>(d.xt0) + static_cast<long>(c0 + j) * mp + r0 + cl, true, 4, v);
+        } else {
+          const long w = static_cast<long>(c0 + j) * np + r0 + cl;
+          store4(d.xm + w, true, 4, v);
+          if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs) + w, true, 4, v);
+        }
+      }
+    }
+
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    if (tid == 0) partials[t] = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kEwThreads) void norm_finalize_kernel(const MatDesc* __restrict__ descs,
+                                                                   const int* __restrict__ prefix,
+                                                                   const float* __restrict__ partials,
+                                                                   MatScale* __restrict__ scales,
+                                                                   float* __restrict__ norms_out) {
+  __shared__ float red[kEwThreads / 64];
+  const int i = blockIdx.x;
+  const int t0 = prefix[i], t1 = prefix[i + 1];
+  float s = 0.0f;
+  for (int t = t0 + threadIdx.x; t < t1; t += kEwThreads) s += partials[t];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float ss = (red[0] + red[1]) + (red[2] + red[3]);
+    const float norm = sqrtf(ss);
+    const float c = 1.0f / (norm + kNormEps);
+    MatScale sc;
+    sc.c = c;
+    sc.c2 = c * c;
+    sc.norm = norm;
+    sc.pad_ = 0.0f;
+    scales[i] = sc;
+    if (norms_out) norms_out[descs[i].out_index] = norm;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __restrict__ descs,
+                                                              const int* __restrict__ prefix, int nmat,
+                                                              int total_tiles, const MatScale* __restrict__ scales,
+                                                              int mode, float lr) {
+  using T = typename Elem<DT>::T;
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  const int tid = threadIdx.x;
+  const int cl = (tid & 15) * 4;
+  const int rl0 = tid >> 4;
+  for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+    const int mi = find_matrix(prefix, nmat, t);
+    const MatDesc& d = descs[mi];
+    if (!d.ns) continue;  // uniform per tile
+    const int local = t - d.ew_tile0;
+    const int tr_ = local / d.ew_tiles_c;
+    const int r0 = tr_ * kEwTile, c0 = (local - tr_ * d.ew_tiles_c) * kEwTile;
+    const int m = d.m, n = d.n, np = d.np;
+    const float sc = scales[mi].c;
+    const float step_lr = -lr * d.lr_scale;
+    if (d.tr) {
+      // caller (r, c) is wide (c, r): stage the wide tile rows c0.., cols r0..
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int j = rl0 + 16 * pass;
+        float v[4];
+        load4(d.xm + static_cast<long>(c0 + j) * np + r0 + cl, true, 4, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[j][cl + e] = v[e];
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rl = rl0 + 16 * pass;
+      const int r = r0 + rl, c = c0 + cl;
+      if (r < m && c < n) {
+        const int valid = min(4, n - c);
+        const bool vec = d.vec_ok && valid == 4;
+        float u[4];
+        if (d.tr) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u[e] = tile[cl + e][rl];
+        } else {
+          load4(d.xm + static_cast<long>(r) * np + c, true, 4, u);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] *= sc;
+        const long o = static_cast<long>(r) * n + c;
+        T* p = static_cast<T*>(d.p) + o;
+        if (mode == kModeMuon) {
+          float pv[4];
+          load4(p, vec, valid, pv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = fmaf(step_lr, u[e], pv[e]);
+          store4(p, vec, valid, pv);
+          if (d.upd) store4(d.upd + o, vec, valid, u);
+        } else {
+          store4(p, vec, valid, u);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prologue(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
+                           float* partials, int mode, float mu, int nesterov, float lr, int grid,
+                           hipStream_t stream) {
+  if (total_tiles <= 0) return hipSuccess;
+  if (dt == kBF16)
+    hipLaunchKernelGGL(prologue_kernel<kBF16>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
+                       total_tiles, partials, mode, mu, nesterov, lr);
+  else
+    hipLaunchKernelGGL(prologue_kernel<kF32>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
+                       total_tiles, partials, mode, mu, nesterov, lr);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const MatDesc* descs, const int* tile_prefix, int nmat, const float* partials,
+                                MatScale* scales, float* norms_out, hipStream_t stream) {
+  if (nmat <= 0) return hipSuccess;
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(nmat), dim3(kEwThreads), 0, stream, descs, tile_prefix, partials,
+                     scales, norms_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_x0(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
+                           const MatScale* scales, int mode, float lr, int grid, hipStream_t stream) {
+  if (total_tiles <= 0) return hipSuccess;
+  if (dt == kBF16)
+    hipLaunchKernelGGL(apply_x0_kernel<kBF16>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
+                       total_tiles, scales, mode, lr);
+  else
+    hipLaunchKernelGGL(apply_x0_kernel<kF32>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
+                       total_tiles, scales, mode, lr);
+  return hipGetLastError();
+}
+
+}  // namespace dmuon

@@ -1,0 +1,167 @@
+"""The C-ABI library: exports, signatures, workspace queries and argument
+validation.  No compute call is made; nothing here needs a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from newton_schulz_08_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dmuon.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmuon_[a-z_0-9]+)\s*\(", text)))
+
+
+def header_defines():
+    return dict(re.findall(r"#define\s+(DMUON_[A-Z_0-9]+)\s+(\d+)", open(HEADER).read()))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    funcs = header_functions()
+    assert len(funcs) >= 9
+    for f in funcs:
+        assert hasattr(lib, f), f"{f} declared in dmuon.h but not exported"
+
+
+def test_binding_signatures_cover_header():
+    assert sorted(_lib.SIGNATURES) == header_functions()
+
+
+def test_constants_match_header():
+    for name, val in header_defines().items():
+        if hasattr(_lib, name):
+            assert getattr(_lib, name) == int(val), name
+    for name in ("DMUON_F32", "DMUON_BF16", "DMUON_OK", "DMUON_ERR_INVALID_ARG", "DMUON_ERR_WORKSPACE",
+                 "DMUON_ERR_NO_DEVICE", "DMUON_MIN_NS_NUMEL"):
+        assert name in header_defines()
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.dmuon_status_string(s).decode() not in ("", "unknown status")
+    assert lib.dmuon_status_string(99).decode() == "unknown status"
+    assert b"gfx950" in lib.dmuon_backend_info()
+
+
+def _ws(lib, shapes, dt=0, fn="dmuon_muon_step_workspace_bytes"):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[s[0] for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[s[1] for s in shapes])
+    out = ctypes.c_size_t(0)
+    st = getattr(lib, fn)(n, rows, cols, dt, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_layout_exact(lib):
+    # one 512x2048 fp32 matrix: descriptor 144 B, prefix 8 B, 256 prologue
+    # tiles (1 KB), scales 16 B -- each region 256-aligned -- then the fp32
+    # iterate (aliased as the Gram operand), two transposed copies and A
+    st, nbytes = _ws(lib, [(512, 2048)], dt=0)
+    assert st == 0
+    mb = 512 * 2048 * 4
+    assert nbytes == 256 + 256 + 1024 + 256 + 3 * mb + 512 * 512 * 4
+    # bf16: fp32 iterate + bf16 operand + 2 bf16 transposed + bf16 Gram
+    st, nb16 = _ws(lib, [(512, 2048)], dt=1)
+    assert nb16 == 256 + 256 + 1024 + 256 + 512 * 2048 * (4 + 2 + 2 + 2) + 512 * 512 * 2
+
+
+def test_workspace_route_and_padding(lib):
+    # 2048x32 (65,536 elements) takes the elementwise route: no NS buffers
+    st, small = _ws(lib, [(2048, 32)])
+    assert st == 0 and small < 64 * 1024
+    # ns_batched orthogonalises every matrix, so the same shape needs buffers
+    st, ns = _ws(lib, [(2048, 32)], fn="dmuon_ns_workspace_bytes")
+    assert st == 0 and ns > 2048 * 256 * 4
+    # ragged shapes pad to 256 in both wide dimensions
+    st, a = _ws(lib, [(300, 700)])
+    st, b = _ws(lib, [(512, 768)])
+    assert a == b
+    st, t = _ws(lib, [(700, 300)])
+    assert t == a
+
+
+def test_workspace_query_errors(lib):
+    assert _ws(lib, [(0, 5)])[0] == _lib.DMUON_ERR_INVALID_ARG
+    assert _ws(lib, [(5, 70000)])[0] == _lib.DMUON_ERR_INVALID_ARG
+    assert _ws(lib, [(5, 5)], dt=7)[0] == _lib.DMUON_ERR_UNSUPPORTED_DTYPE
+    assert _ws(lib, [])[0] == 0 and _ws(lib, [])[1] == 0
+    rows = (ctypes.c_int64 * 1)(4)
+    assert lib.dmuon_muon_step_workspace_bytes(1, rows, rows, 0, None) == _lib.DMUON_ERR_INVALID_ARG
+
+
+def _step(lib, count=1, shapes=((64, 64),), ptrs=None, dt=0, steps=5, mu=0.95, lr=0.02, ws=None, wsb=0,
+          upd=None):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[s[0] for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[s[1] for s in shapes])
+    base = 0x10000000
+    if ptrs is None:
+        ptrs = ([base + 0x100000 * i for i in range(n)], [base + 0x100000 * (i + n) for i in range(n)],
+                [base + 0x100000 * (i + 2 * n) for i in range(n)])
+    P = lambda v: (ctypes.c_void_p * max(n, 1))(*v)  # noqa: E731
+    return lib.dmuon_muon_step(count, P(ptrs[0]), P(ptrs[1]), P(ptrs[2]), rows, cols, dt, steps,
+                               ctypes.c_float(mu), 1, ctypes.c_float(lr), None, upd, None,
+                               ctypes.c_void_p(ws), wsb, None)
+
+
+def test_validation_before_any_device_work(lib):
+    E = _lib
+    assert _step(lib, count=-1) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, count=0) == E.DMUON_OK
+    assert _step(lib, shapes=((0, 4),)) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, dt=3) == E.DMUON_ERR_UNSUPPORTED_DTYPE
+    assert _step(lib, steps=-1) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, steps=65) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, mu=float("nan")) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, lr=float("inf")) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, ptrs=([0], [0x2000], [0x3000])) == E.DMUON_ERR_INVALID_ARG
+    assert "params[0] is NULL" in _lib.last_error()
+    assert _step(lib, ptrs=([0x1000], [0x1000], [0x3000])) == E.DMUON_ERR_INVALID_ARG
+    assert "alias" in _lib.last_error()
+    two = ((64, 64), (64, 64))
+    assert _step(lib, count=2, shapes=two, ptrs=([0x1000, 0x1000], [0x2000, 0x2100], [0x3000, 0x3100])) == \
+        E.DMUON_ERR_INVALID_ARG
+    # workspace missing / short / misaligned
+    assert _step(lib, ws=None) == E.DMUON_ERR_WORKSPACE
+    assert _step(lib, ws=0x100000, wsb=16) == E.DMUON_ERR_WORKSPACE
+    st, need = _ws(lib, [(64, 64)])
+    assert _step(lib, ws=0x100010, wsb=need) == E.DMUON_ERR_WORKSPACE
+    assert "aligned" in _lib.last_error()
+
+
+def test_ns_batched_validation(lib):
+    rows = (ctypes.c_int64 * 2)(8, 8)
+    P = (ctypes.c_void_p * 2)
+    E = _lib
+    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x3000), rows, rows, 0, 5, None, 0, None) == \
+        E.DMUON_ERR_INVALID_ARG
+    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x4000), rows, rows, 0, -2, None, 0, None) == \
+        E.DMUON_ERR_INVALID_ARG
+    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x4000), rows, rows, 0, 5, None, 0, None) == \
+        E.DMUON_ERR_WORKSPACE
+    assert lib.dmuon_ns_batched(0, None, None, None, None, 0, 5, None, 0, None) == E.DMUON_OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path; a GPU is visible")
+def test_no_device_reported(lib):
+    st, need = _ws(lib, [(64, 64)])
+    assert _step(lib, ws=0x10000000, wsb=need) == _lib.DMUON_ERR_NO_DEVICE
+
+
+def test_profile_read_empty(lib):
+    stats = (_lib.KernelStat * 4)()
+    n = ctypes.c_int(-1)
+    assert lib.dmuon_profile_read(stats, 4, ctypes.byref(n)) == 0
+    assert n.value == 0

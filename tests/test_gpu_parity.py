@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element on seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import newton_schulz_08_amd as nsa
+from workloads import gen
+from workloads.configs import MatrixSpec, SetConfig, get_config
+
+from gpu_util import (TOL, TORCH_DT, check_update_faithful, f32_mu, max_ulp_err_f32, rel_fro, to_device,
+                      to_host_f64, ulp)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    nsa.load()
+    print("backend:", nsa.backend_info(), flush=True)
+
+
+def _adhoc(shapes, dtype, cfg_id, grad_dist="normal", grad_scale=1.0):
+    return SetConfig(key=f"adhoc{cfg_id}", cfg_id=cfg_id,
+                     matrices=tuple(MatrixSpec(f"m{i}", r, c) for i, (r, c) in enumerate(shapes)),
+                     dtype=dtype, grad_dist=grad_dist, grad_scale=grad_scale, weight_scale=1.0)
+
+
+def run_muon(cfg, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.02, lr_scale=None, nonzero_buf=False,
+             with_update=True):
+    """One dmuon_muon_step over every matrix of cfg; returns host copies."""
+    n = cfg.count
+    g = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(n)]
+    p = [gen.draw_matrix(cfg, i, gen.WEIGHT) for i in range(n)]
+    b = [gen.draw_matrix(cfg, i, gen.MOMENTUM) if nonzero_buf else None for i in range(n)]
+    dg = [to_device(x) for x in g]
+    dp = [to_device(x) for x in p]
+    db = [to_device(x) if x is not None else torch.zeros(x_.values.shape, dtype=torch.float32, device="cuda")
+          for x, x_ in zip(b, g)]
+    du = [torch.full(x.values.shape, float("nan"), dtype=torch.float32, device="cuda") for x in g] \
+        if with_update else None
+    norms = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    nsa.muon_step(dp, dg, db, ns_steps=ns_steps, mu=mu, nesterov=nesterov, lr=lr, lr_scale=lr_scale,
+                  update_out=du, norms_out=norms)
+    torch.cuda.synchronize()
+    return dict(
+        g=[x.as_f64() for x in g], p0=[x.as_f64() for x in p],
+        b0=[x.as_f64() if x is not None else np.zeros(x_.values.shape) for x, x_ in zip(b, g)],
+        p=[to_host_f64(t) for t in dp], b=[to_host_f64(t) for t in db],
+        u=[to_host_f64(t) for t in du] if with_update else None,
+        norms=norms.cpu().numpy().astype(np.float64))
+
+
+def check_against_oracle(cfg, res, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.02, lr_scale=None,
+                         indices=None):
+    dtype = cfg.dtype
+    mu32 = f32_mu(mu)
+    indices = range(cfg.count) if indices is None else indices
+    worst = 0.0
+    for i in indices:
+        spec = cfg.matrices[i]
+        s = 1.0 if lr_scale is None else float(lr_scale[i])
+        pw, bw, uw, nw = oracle.muon_step([res["p0"][i]], [res["g"][i]], [res["b0"][i]], mu32, nesterov,
+                                          ns_steps, lr, [s])
+        # momentum: one fused multiply-add in fp32 -> within one fp32 ulp
+        e = max_ulp_err_f32(res["b"][i], bw[0])
+        assert e <= 1.0, f"{spec.name}: momentum off by {e:.2f} ulp"
+        assert abs(res["norms"][i] - nw[0]) <= 1e-5 * nw[0] + 1e-30, (spec.name, res["norms"][i], nw[0])
+        if res["u"] is not None:
+            u = res["u"][i]
+            assert np.all(np.isfinite(u)), spec.name
+            if spec.numel < oracle.MIN_NS_NUMEL:
+                # U = fma(mu, buf', g) rounded once, from the GPU's own buf'
+                y_exact = res["g"][i] + mu32 * res["b"][i] if nesterov else res["b"][i]
+                eu = max_ulp_err_f32(u, y_exact)
+                assert eu <= 1.0, f"{spec.name}: elementwise-route update off by {eu:.2f} ulp"
+                # against the oracle: buf' rounding (<= 1 ulp) propagates through mu
+                bound = mu32 * ulp(bw[0], "f32") + ulp(uw[0], "f32")
+                assert np.all(np.abs(u - uw[0]) <= bound * 1.0000001), spec.name
+            else:
+                err = rel_fro(u, uw[0])
+                worst = max(worst, err)
+                assert err <= TOL[dtype], f"{spec.name} {spec.rows}x{spec.cols}: rel err {err:.3e} > {TOL[dtype]}"
+            check_update_faithful(res["p"][i], res["p0"][i], u, lr, s, dtype)
+    return worst
+
+
+# ------------------------------------------------------------------ small / ragged
+RAGGED = [(600, 1100), (1100, 600), (300, 700), (257, 1000), (1000, 130), (250, 400), (3, 33333),
+          (50, 70), (2048, 32), (512, 512)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_batch(dtype):
+    cfg = _adhoc(RAGGED, dtype, 101 if dtype == "f32" else 102)
+    res = run_muon(cfg)
+    worst = check_against_oracle(cfg, res)
+    print(f"ragged {dtype}: worst NS rel err {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_nonzero_momentum_and_lr_scale(dtype, nesterov):
+    shapes = [(384, 640), (640, 384), (40, 60)]
+    cfg = _adhoc(shapes, dtype, 110 + (dtype == "bf16") * 2 + nesterov)
+    scale = [oracle.moonlight_lr_scale(r, c) for r, c in shapes]
+    res = run_muon(cfg, nonzero_buf=True, nesterov=nesterov, lr_scale=scale, mu=0.9, lr=0.01)
+    check_against_oracle(cfg, res, nesterov=nesterov, lr_scale=scale, mu=0.9, lr=0.01)
+
+
+@pytest.mark.parametrize("steps", [0, 1, 2, 7])
+def test_step_counts(steps):
+    cfg = _adhoc([(512, 768), (768, 512)], "f32", 120 + steps)
+    res = run_muon(cfg, ns_steps=steps)
+    check_against_oracle(cfg, res, ns_steps=steps)
+
+
+def test_worked_example_small_route(golden):
+    fx = golden("momentum_worked_example.txt")
+    for dt in (torch.float32, torch.bfloat16):
+        for nesterov, tag in ((True, "nesterov"), (False, "plain")):
+            t = lambda k, d=dt: torch.tensor(fx[k], dtype=d, device="cuda").reshape(2, 2)  # noqa: E731
+            p, g, b = t("p0"), t("grad"), t("buf0", torch.float32)
+            u = torch.empty(2, 2, dtype=torch.float32, device="cuda")
+            nsa.muon_step([p], [g], [b], ns_steps=5, mu=fx["mu"][0], nesterov=nesterov, lr=fx["lr"][0],
+                          update_out=[u])
+            torch.cuda.synchronize()
+            assert b.cpu().flatten().tolist() == fx["buf1"]
+            assert u.cpu().flatten().tolist() == fx["y_" + tag]
+            assert p.float().cpu().flatten().tolist() == fx["p1_" + tag]
+
+
+def test_zero_gradient_gives_zero_update():
+    for dt in (torch.float32, torch.bfloat16):
+        g = torch.zeros(512, 1024, dtype=dt, device="cuda")
+        p = torch.randn(512, 1024, device="cuda").to(dt)
+        p0 = p.clone()
+        b = torch.zeros(512, 1024, device="cuda")
+        u = torch.full((512, 1024), float("nan"), device="cuda")
+        norms = torch.full((1,), float("nan"), device="cuda")
+        nsa.muon_step([p], [g], [b], update_out=[u], norms_out=norms)
+        torch.cuda.synchronize()
+        assert torch.equal(p, p0)
+        assert torch.count_nonzero(u).item() == 0
+        assert norms.item() == 0.0
+
+
+def test_empty_batch_is_noop():
+    assert nsa.ns_batched([]) == []
+    lib = nsa.load()
+    assert lib.dmuon_muon_step(0, None, None, None, None, None, 0, 5, 0.95, 1, 0.02, None, None, None, None, 0,
+                               None) == 0
+
+
+def test_route_boundary():
+    # 99,999 elements -> elementwise; 100,000 -> Newton-Schulz
+    cfg = _adhoc([(3, 33333), (250, 400), (400, 250)], "f32", 130)
+    res = run_muon(cfg)
+    check_against_oracle(cfg, res)
+    u_small = res["u"][0]
+    y = res["g"][0] * (1.0 + f32_mu(0.95))
+    assert max_ulp_err_f32(u_small, y) <= 1.0
+
+
+# ------------------------------------------------------------------ determinism / invariance
+def test_bitwise_determinism_and_batch_invariance():
+    shapes = [(512, 1024), (1024, 512), (256, 300)]
+    cfg = _adhoc(shapes, "bf16", 140)
+    g = [to_device(gen.draw_matrix(cfg, i, gen.GRAD)) for i in range(3)]
+    p0 = [to_device(gen.draw_matrix(cfg, i, gen.WEIGHT)) for i in range(3)]
+
+    def once(idx):
+        p = [p0[i].clone() for i in idx]
+        b = [torch.zeros(shapes[i], device="cuda") for i in idx]
+        u = [torch.empty(shapes[i], device="cuda") for i in idx]
+        nsa.muon_step(p, [g[i] for i in idx], b, update_out=u)
+        torch.cuda.synchronize()
+        return p, b, u
+
+    pa, ba, ua = once([0, 1, 2])
+    pb, bb, ub = once([0, 1, 2])
+    pc, bc, uc = once([2, 0])
+    for x, y in zip(pa + ba + ua, pb + bb + ub):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x, y.view(torch.uint8)
+                           if y.dtype == torch.bfloat16 else y)
+    assert torch.equal(ua[2], uc[0]) and torch.equal(ua[0], uc[1])
+    assert torch.equal(pa[2].view(torch.int16), pc[0].view(torch.int16))
+
+
+def test_update_out_does_not_change_params():
+    shapes = [(512, 768), (768, 512), (30, 40)]
+    cfg = _adhoc(shapes, "bf16", 150)
+    g = [to_device(gen.draw_matrix(cfg, i, gen.GRAD)) for i in range(3)]
+    p0 = [to_device(gen.draw_matrix(cfg, i, gen.WEIGHT)) for i in range(3)]
+    outs = []
+    for with_u in (False, True):
+        p = [x.clone() for x in p0]
+        b = [torch.zeros(s, device="cuda") for s in shapes]
+        u = [torch.empty(s, device="cuda") for s in shapes] if with_u else None
+        nsa.muon_step(p, g, b, update_out=u)
+        torch.cuda.synchronize()
+        outs.append(p)
+    for x, y in zip(*outs):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_two_steps_nesterov():
+    """Two consecutive steps from a zero buffer (distinguishes the Nesterov
+    readings: the second step's input is G2 + mu (mu G1 + G2))."""
+    shapes = [(512, 640), (640, 512)]
+    cfg = _adhoc(shapes, "f32", 160)
+    g1 = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(2)]
+    g2 = [gen.draw_matrix(cfg, i, gen.GRAD2) for i in range(2)]
+    p0 = [gen.draw_matrix(cfg, i, gen.WEIGHT) for i in range(2)]
+    dp = [to_device(x) for x in p0]
+    db = [torch.zeros(s, device="cuda") for s in shapes]
+    du = [torch.empty(s, device="cuda") for s in shapes]
+    step = nsa.MuonStep(dp, [to_device(x) for x in g1], db, update_out=du)
+    step()
+    dg2 = [to_device(x) for x in g2]
+    step2 = nsa.MuonStep(dp, dg2, db, update_out=du, workspace=step.workspace)
+    step2()
+    torch.cuda.synchronize()
+    mu = f32_mu(0.95)
+    for i in range(2):
+        pw, bw, uw, _ = oracle.muon_step([p0[i].as_f64()], [g1[i].as_f64()], [np.zeros(shapes[i])], mu, True, 5,
+                                         0.02)
+        pw, bw, uw, _ = oracle.muon_step(pw, [g2[i].as_f64()], bw, mu, True, 5, 0.02)
+        assert rel_fro(to_host_f64(du[i]), uw[0]) <= TOL["f32"]
+        assert max_ulp_err_f32(to_host_f64(db[i]), bw[0]) <= 2.0
+        assert rel_fro(to_host_f64(dp[i]), pw[0]) < 1e-6
+
+
+# ------------------------------------------------------------------ ns_batched
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ns_batched_ragged(dtype):
+    shapes = [(300, 700), (700, 300), (40, 50), (256, 256), (520, 1030)]
+    cfg = _adhoc(shapes, dtype, 170 + (dtype == "bf16"))
+    xs = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(len(shapes))]
+    outs = nsa.ns_batched([to_device(x) for x in xs], ns_steps=5)
+    torch.cuda.synchronize()
+    for x, o, s in zip(xs, outs, shapes):
+        err = rel_fro(to_host_f64(o), oracle.newton_schulz(x.as_f64(), 5))
+        assert err <= TOL[dtype], (s, err)
+
+
+def test_ns_batched_in_place():
+    x = torch.randn(384, 896, device="cuda")
+    ref = nsa.ns_batched([x.clone()], ns_steps=5)[0]
+    nsa.ns_batched([x], [x], ns_steps=5)
+    torch.cuda.synchronize()
+    assert torch.equal(x, ref)
+
+
+def test_ns_rejects_bad_input():
+    with pytest.raises(ValueError):
+        nsa.ns_batched([torch.randn(16, device="cuda")])
+    with pytest.raises(TypeError):
+        nsa.ns_batched([torch.randn(16, 16, device="cuda", dtype=torch.float16)])
