@@ -22,6 +22,8 @@
 // register staging) while the current stage is multiplied.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,7 +34,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int kStageBytes = 65536;   // P (32 KB) + Q (32 KB)
 constexpr int kOperandBytes = 32768; // 256 rows x 128 bytes
 
@@ -44,13 +45,23 @@ __device__ __forceinline__ float to_f32(__bf16 v) { return static_cast<float>(v)
 __device__ __forceinline__ float to_f32(float v) { return v; }
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
 
-// Map a workgroup id to a logical tile so that each XCD (workgroups are
-// dispatched round-robin over the 8 XCDs) walks one contiguous range of the
-// logical order, keeping operands that neighbouring tiles share in its own L2.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-  const int per = total / 8, rem = total % 8;
-  const int x = b % 8, slot = b / 8;
-  return (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Within a segment of n tiles whose blocks start at t0, give each XCD
+// one contiguous n/8 share of the segment's tile order, so every XCD gets the
+// same mix of long and short tiles and neighbouring tiles (which share
+// operand panels) meet in the same L2.  Returns the tile index for block
+// t0 + local; a bijection on [0, n).
+__device__ __forceinline__ int xcd_share(int local, int n, int t0) {
+  const int x = (t0 + local) & 7;
+  int off = 0, first_x = 0;
+#pragma unroll
+  for (int y = 0; y < 8; ++y) {
+    const int f = (y - (t0 & 7) + 8) & 7;  // first local index placed on XCD y
+    const int cnt = f < n ? (n - f + 7) >> 3 : 0;
+    if (y < x) off += cnt;
+    if (y == x) first_x = f;
+  }
+  return off + ((local - first_x) >> 3);
 }
 
 struct TileRef {
@@ -60,11 +71,11 @@ struct TileRef {
   int kdim;
 };
 
-__device__ __forceinline__ TileRef locate(const SegTable& st, int logical, bool lower) {
+__device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lower) {
   int si = 0;
-  while (si + 1 < st.nseg && st.seg[si + 1].tile0 <= logical) ++si;
+  while (si + 1 < st.nseg && st.seg[si + 1].tile0 <= block) ++si;
   const Segment& sg = st.seg[si];
-  const int local = logical - sg.tile0;
+  const int local = xcd_share(block - sg.tile0, sg.ntiles, sg.tile0);
   TileRef r;
   r.mat = sg.mat0 + local / sg.tiles_per_mat;
   const int t = local % sg.tiles_per_mat;
@@ -91,108 +102,290 @@ __device__ __forceinline__ TileRef locate(const SegTable& st, int logical, bool 
   return r;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
+typedef __attribute__((address_space(3))) char* lds_cptr_t;
+
+// Byte address of a __shared__ location in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_address(char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_cptr_t)p));  // address-space cast
+}
+
+// A workgroup-uniform pointer moved into SGPRs (it is computed from the block
+// index and descriptor fields, but not always provably uniform to the compiler).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// global_load_lds_dwordx4: 16 bytes from base + voff (per lane) to
+// LDS[lds_dst + 16 * lane].  Issued through asm so the compiler's wait-count
+// pass does not treat it as an LDS operation of unknown completion order
+// (which would force a full LDS wait before every fragment use); callers wait
+// with an explicit vmcnt(0) and a barrier before reading the data.  M0 is set
+// here and used by nothing else in these kernels; s_nop covers the M0 hazard.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "s"(lds_dst)
+               : "memory");
+}
+
+// Wave grid of a 256x256 tile: 2 waves along M (128 rows each) and
+// kWaves / 2 along N; each wave owns kBM x kBN blocks of 32x32.
+template <int kWaves>
+struct WaveGrid {
+  static constexpr int kThreadsPerBlock = 64 * kWaves;
+  static constexpr int kWN = kWaves / 2;
+  static constexpr int kBM = 4;                    // 128 rows
+  static constexpr int kBN = 256 / kWN / 32;       // 128 (4 waves) or 64 (8 waves) cols
+  static constexpr int kLoadsPerOperand = 256 / kWaves / 8;  // 8-row wave loads per operand
+};
 
 // Accumulate the 256x256 tile of P * Q^T into acc.  P0/Q0 point at the first
 // row of each 256-row panel; ld*_bytes are row pitches; kbytes the contraction
 // length in bytes (a multiple of 128).
 //
 // Global -> LDS: global_load_lds_dwordx4 writes lane l's 16 bytes to
-// LDS[M0 + 16 l], so one wave instruction fills 8 rows x 128 bytes.  Lane l
-// fetches chunk (l & 7) ^ (row & 7) of its row, which stores the tile in the
-// XOR-swizzled layout the fragment reads expect, with no VGPR staging.  Each
-// wave loads rows [64 w, 64 w + 64) of both operands (8 + 8 instructions per
-// stage).
-template <int DT>
-__device__ __forceinline__ void block_product(const char* __restrict__ P0, long ldp_bytes,
-                                              const char* __restrict__ Q0, long ldq_bytes,
-                                              int kbytes, char* lds, f32x16 (&acc)[4][4]) {
+// LDS[M0 + 16 l], so one wave instruction fills 8 rows x 128 bytes.  Each lane
+// fetches the source chunk that belongs in its slot of the XOR-swizzled
+// layout the fragment reads expect, so there is no VGPR staging.  Wave w
+// loads rows [w * 256 / kWaves, (w + 1) * 256 / kWaves) of both operands.
+template <int DT, int kWaves>
+__device__ __forceinline__ void block_product(const char* __restrict__ P0, int ldp_bytes,
+                                              const char* __restrict__ Q0, int ldq_bytes, int kbytes, char* lds,
+                                              f32x16 (&acc)[4][WaveGrid<kWaves>::kBN]) {
+  using G = WaveGrid<kWaves>;
+  constexpr int kBN = G::kBN;
+  constexpr int kRowsPerWave = 256 / kWaves;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave / G::kWN, wc = wave % G::kWN;
   const int li = lane & 31, lh = lane >> 5;
 
+  // Row r of a stage stores logical 16-byte chunk c at slot c ^ swz(r) with
+  // swz(r) = (r & 7) ^ ((r >> 3) & 1): the 16 lanes an LDS cycle serves for
+  // ds_read_b128 (rows r..r+15, 64 banks) and any 8 consecutive rows then hit
+  // distinct banks.  The wave's 8-row load groups start at multiples of 8, so
+  // for load group u the swizzle is lrow ^ (u & 1).
+  P0 = uniform_ptr(P0);
+  Q0 = uniform_ptr(Q0);
   const int lrow = lane >> 3;                    // row within an 8-row group
-  const int lchunk = (lane & 7) ^ lrow;          // source chunk for the swizzled slot
-  const char* gp = P0 + static_cast<long>(wave * 64 + lrow) * ldp_bytes + lchunk * 16;
-  const char* gq = Q0 + static_cast<long>(wave * 64 + lrow) * ldq_bytes + lchunk * 16;
-  const long grp_p = 8L * ldp_bytes, grp_q = 8L * ldq_bytes;
-  char* lds_wave = lds + wave * 64 * 128;
+  const int lchunk0 = (lane & 7) ^ lrow;         // source chunk, even load groups
+  const int lchunk1 = lchunk0 ^ 1;               // odd load groups
+  const uint32_t rp = static_cast<uint32_t>((wave * kRowsPerWave + lrow) * ldp_bytes);
+  const uint32_t rq = static_cast<uint32_t>((wave * kRowsPerWave + lrow) * ldq_bytes);
+  const uint32_t offp0 = rp + lchunk0 * 16, offp1 = rp + lchunk1 * 16;
+  const uint32_t offq0 = rq + lchunk0 * 16, offq1 = rq + lchunk1 * 16;
+  const uint32_t grp_p = static_cast<uint32_t>(8 * ldp_bytes), grp_q = static_cast<uint32_t>(8 * ldq_bytes);
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * kRowsPerWave * 128);
 
   auto issue = [&](int stage, int kb) {
-    char* dp = lds_wave + stage * kStageBytes;
+    const uint32_t dp = lds_wave + stage * kStageBytes;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gp + u * grp_p + kb), (lds_ptr_t)(dp + u * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gq + u * grp_q + kb), (lds_ptr_t)(dp + kOperandBytes + u * 1024),
-                                       16, 0, 0);
+    for (int u = 0; u < G::kLoadsPerOperand; ++u) {
+      lds_dma16(P0, ((u & 1) ? offp1 : offp0) + u * grp_p + kb, dp + u * 1024);
+      lds_dma16(Q0, ((u & 1) ? offq1 : offq0) + u * grp_q + kb, dp + kOperandBytes + u * 1024);
     }
   };
 
-  // fragment reads: row (block * 32 + li), chunk (2 s + lh) ^ (li & 7)
+  // fragment reads: row (block * 32 + li), logical chunk 2 s + lh
   const int frag_row = li * 128;
-  const int sw = li & 7;
+  const int sw = (li & 7) ^ ((li >> 3) & 1);
 
+  // Fragments: per sub-step s (16 bf16 / 4x4 fp32 of K) a wave needs 4 row
+  // fragments of P and kBN of Q; two register slots alternate between
+  // sub-steps.  sched_barrier(0) fences pin the software pipeline: the reads
+  // of sub-step s + 1 are issued before the MFMAs of sub-step s, and the
+  // stage barrier sits before the last sub-step's MFMAs so the next stage's
+  // first fragments load while they run.
+  using Frag = typename std::conditional<DT == kBF16, bf16x8, f32x4>::type;
+  Frag fa[2][4], fb[2][kBN];
+  auto read_frags = [&](int stage, int s, int slot) {
+    const char* sp = lds + stage * kStageBytes + wr * 128 * 128 + frag_row;
+    const char* sq = lds + stage * kStageBytes + kOperandBytes + wc * (kBN * 32) * 128 + frag_row;
+    const int co = (((2 * s + lh) ^ sw) << 4);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) fa[slot][x] = *reinterpret_cast<const Frag*>(sp + x * 32 * 128 + co);
+#pragma unroll
+    for (int x = 0; x < kBN; ++x) fb[slot][x] = *reinterpret_cast<const Frag*>(sq + x * 32 * 128 + co);
+  };
+  auto mfmas = [&](int slot) {
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kBN; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][ni], fa[slot][mi], acc[mi][ni], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < kBN; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[slot][ni][e], fa[slot][mi][e], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  // Pipeline: stage kt is multiplied from buffer kt & 1 while stage kt + 1
+  // lands in the other buffer.  Loads for stage kt + 2 are issued right after
+  // the barrier that ends stage kt's fragment reads, into the buffer stage kt
+  // just released, so each load has a full stage to land.  Issuing them there,
+  // after the barrier's full wait, also keeps the LDS-read waits before each
+  // MFMA group partial (the compiler counts the LDS-DMA loads conservatively).
   const int nk = kbytes / 128;
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  issue(1, min(1, nk - 1) * 128);
+  read_frags(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    // branch-free body: the last iteration re-loads the final stage into the
-    // idle buffer (in bounds, never read) so the loop stays one basic block
-    const int next_kb = min(kt + 1, nk - 1) * 128;
-    const char* sp = lds + (kt & 1) * kStageBytes + wr * 128 * 128 + frag_row;
-    const char* sq = lds + (kt & 1) * kStageBytes + kOperandBytes + wc * 128 * 128 + frag_row;
-    if constexpr (DT == kBF16) {
-      // fragments of sub-step s + 1 are read while sub-step s multiplies
-      bf16x8 a[2][4], b[2][4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        a[0][x] = *reinterpret_cast<const bf16x8*>(sp + x * 32 * 128 + ((lh ^ sw) << 4));
-        b[0][x] = *reinterpret_cast<const bf16x8*>(sq + x * 32 * 128 + ((lh ^ sw) << 4));
-      }
-      issue((kt + 1) & 1, next_kb);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < 4) {
-          const int co = (((2 * (s + 1) + lh) ^ sw) << 4);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            a[cur ^ 1][x] = *reinterpret_cast<const bf16x8*>(sp + x * 32 * 128 + co);
-            b[cur ^ 1][x] = *reinterpret_cast<const bf16x8*>(sq + x * 32 * 128 + co);
-          }
-        }
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mi], b[cur][ni], acc[mi][ni], 0, 0, 0);
-      }
-    } else {
-      issue((kt + 1) & 1, next_kb);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int co = (((2 * s + lh) ^ sw) << 4);
-        f32x4 a[4], b[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          a[x] = *reinterpret_cast<const f32x4*>(sp + x * 32 * 128 + co);
-          b[x] = *reinterpret_cast<const f32x4*>(sq + x * 32 * 128 + co);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mi][e], b[ni][e], acc[mi][ni], 0, 0, 0);
-      }
-    }
+    const int c = kt & 1;
+    read_frags(c, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(c, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(c, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // branch-free: past the end the final stage is re-loaded into the idle
+    // buffer (in bounds, never used) so the loop body stays one basic block
+    issue(c, min(kt + 2, nk - 1) * 128);
+    read_frags(c ^ 1, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+#ifndef DMUON_WAVES
+#define DMUON_WAVES 8
+#endif
+constexpr int kWaves = DMUON_WAVES;
+using Grid = WaveGrid<kWaves>;
+constexpr int kBN = Grid::kBN;
+constexpr int kThreads = Grid::kThreadsPerBlock;
+
+// ---------------------------------------------------------------- epilogue
+// The MFMAs take (Q, P) so each accumulator block holds the transposed
+// product: lane (li, lh), register 4 g + q of block (mi, ni) is
+//   C[32 mi + li][32 (wc kBN + ni) + 8 g + 4 lh + q]
+// (rows relative to the wave's 128-row half), i.e. four consecutive columns of
+// one row.  The epilogue stages one 128 x 256 fp32 half-tile at a time in the
+// 128 KB of LDS the operand stages no longer need, then writes every output
+// with 16-byte lanes: rows for row-major outputs, 8-row column segments for
+// transposed ones.
+//
+// Staging layout: 16-byte chunk c (0..63) of row r (0..127) lives at chunk
+// c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 63.  Conflict-free for the three
+// patterns used: fragment stores (16 rows x one chunk), row reads (one row x
+// 64 chunks) and column reads (rows 8 s + i, s = 0..15, four adjacent columns).
+__device__ __forceinline__ int stage_off(int r, int c) { return r * 1024 + ((c ^ ((r ^ (r >> 3)) & 63)) << 4); }
+
+__device__ __forceinline__ void stage_acc(char* lds, const f32x16 (&acc)[4][kBN], float scale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, lh = lane >> 5;
+  const int cbase = (wave % Grid::kWN) * kBN * 8;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kBN; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 v = make_float4(acc[mi][ni][4 * g] * scale, acc[mi][ni][4 * g + 1] * scale,
+                                     acc[mi][ni][4 * g + 2] * scale, acc[mi][ni][4 * g + 3] * scale);
+        *reinterpret_cast<float4*>(lds + stage_off(32 * mi + li, cbase + 8 * ni + 2 * g + lh)) = v;
+      }
+}
+
+__device__ __forceinline__ float4 stage_ld4(const char* lds, int r, int c) {
+  return *reinterpret_cast<const float4*>(lds + stage_off(r, c));
+}
+__device__ __forceinline__ void stage_st4(char* lds, int r, int c, float4 v) {
+  *reinterpret_cast<float4*>(lds + stage_off(r, c)) = v;
+}
+// Column segment: rows 8 s .. 8 s + 7 of column col.
+__device__ __forceinline__ void stage_col8(const char* lds, int s, int col, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = *reinterpret_cast<const float*>(lds + stage_off(8 * s + i, col >> 2) + (col & 3) * 4);
+}
+
+// 4 / 8 consecutive elements of T to and from fp32 (16-byte aligned vectors).
+__device__ __forceinline__ void vst4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void vst4(__bf16* p, const float* v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = static_cast<__bf16>(v[e]);
+  *reinterpret_cast<bf16x4*>(p) = x;
+}
+__device__ __forceinline__ void vld4(const float* p, float* v) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+__device__ __forceinline__ void vld4(const __bf16* p, float* v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(x[e]);
+}
+__device__ __forceinline__ void vst8(float* p, const float* v) { vst4(p, v); vst4(p + 4, v + 4); }
+__device__ __forceinline__ void vst8(__bf16* p, const float* v) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  bf16x8_t x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(v[e]);
+  *reinterpret_cast<bf16x8_t*>(p) = x;
+}
+
+// Last Newton-Schulz step: N consecutive elements of U at caller (orow,
+// ocol0 ..) -> p -= lr*s*U (+ update_out) or out = U, masked to the caller's
+// shape; 4-element vectors where the row layout and pointers allow it.
+template <typename T, int N>
+__device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float step_lr, int orow, int ocol0,
+                                             const float* u) {
+  if (orow >= d.m) return;
+  const long o = static_cast<long>(orow) * d.n + ocol0;
+  T* p = static_cast<T*>(d.p) + o;
+  float* upd = d.upd ? d.upd + o : nullptr;
+#pragma unroll
+  for (int h4 = 0; h4 < N; h4 += 4) {
+    const int c = ocol0 + h4;
+    if (d.vec_ok && c + 4 <= d.n) {
+      float v[4];
+      if (mode == kModeMuon) {
+        vld4(p + h4, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(step_lr, u[h4 + e], v[e]);
+        vst4(p + h4, v);
+        if (upd) vst4(upd + h4, u + h4);
+      } else {
+        vst4(p + h4, u + h4);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c + e >= d.n) break;
+        if (mode == kModeMuon) {
+          p[h4 + e] = static_cast<T>(fmaf(step_lr, u[h4 + e], static_cast<float>(p[h4 + e])));
+          if (upd) upd[h4 + e] = u[h4 + e];
+        } else {
+          p[h4 + e] = static_cast<T>(u[h4 + e]);
+        }
+      }
+    }
   }
 }
 
@@ -203,48 +396,51 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   constexpr int EB = Elem<DT>::kBytes;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const TileRef tr = locate(st, logical, true);
+  const TileRef tr = locate(st, blockIdx.x, true);
   const MatDesc& d = descs[tr.mat];
   const int mp = d.mp, np = d.np;
   const char* xs = static_cast<const char*>(d.xs);
   const long ld = static_cast<long>(np) * EB;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kBN];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16{};
+    for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
-  block_product<DT>(xs + static_cast<long>(tr.bi) * kTile * ld, ld, xs + static_cast<long>(tr.bj) * kTile * ld, ld,
-                    np * EB, lds, acc);
+  block_product<DT, kWaves>(xs + static_cast<long>(tr.bi) * kTile * ld, ld, xs + static_cast<long>(tr.bj) * kTile * ld,
+                            ld, np * EB, lds, acc);
 
   const float alpha = first_step ? scales[tr.mat].c2 : 1.0f;
   T* a = static_cast<T*>(d.a);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lh = lane >> 5;
-  const int R0 = tr.bi * kTile + wr * 128, C0 = tr.bj * kTile + wc * 128;
+  const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
+  const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
   const bool mirror = tr.bi != tr.bj;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = C0 + ni * 32 + li;
-        const int row0 = R0 + mi * 32 + 8 * g + 4 * lh;
-        T v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = from_f32<T>(acc[mi][ni][4 * g + q] * alpha);
-          a[static_cast<long>(row0 + q) * mp + col] = v[q];
-        }
-        if (mirror) {
-          T* dst = a + static_cast<long>(col) * mp + row0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[q] = v[q];
-        }
+  __syncthreads();  // operand stages are free
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (wr == h) stage_acc(lds, acc, alpha);
+    __syncthreads();
+    // A rows: thread covers chunk tid & 63 of rows (tid >> 6) + 8 k
+#pragma unroll 4
+    for (int k = 0; k < (128 * 64 / kThreads); ++k) {
+      const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
+      const float4 v4 = stage_ld4(lds, r, c);
+      const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+      vst4(a + static_cast<long>(Rt + 128 * h + r) * mp + Ct + 4 * c, v);
+    }
+    if (mirror) {
+      // transposed copy into the upper triangle: 8-row segments of columns
+#pragma unroll 2
+      for (int j = 0; j < (256 * 16 / kThreads); ++j) {
+        const int q = tid + kThreads * j, sgi = q & 15, col = q >> 4;
+        float v[8];
+        stage_col8(lds, sgi, col, v);
+        vst8(a + static_cast<long>(Ct + col) * mp + Rt + 128 * h + 8 * sgi, v);
       }
+    }
+    __syncthreads();
+  }
 }
 
 template <int DT>
@@ -255,87 +451,72 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   constexpr int EB = Elem<DT>::kBytes;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const TileRef tr = locate(st, logical, false);
+  const TileRef tr = locate(st, blockIdx.x, false);
   const MatDesc& d = descs[tr.mat];
   const int mp = d.mp, np = d.np;
   const char* a = static_cast<const char*>(d.a);
   const char* xt_in = static_cast<const char*>((step & 1) ? d.xt1 : d.xt0);
   const long lda = static_cast<long>(mp) * EB;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kBN];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16{};
+    for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
-  block_product<DT>(a + static_cast<long>(tr.bi) * kTile * lda, lda, xt_in + static_cast<long>(tr.bj) * kTile * lda,
-                    lda, mp * EB, lds, acc);
+  block_product<DT, kWaves>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
+                            xt_in + static_cast<long>(tr.bj) * kTile * lda, lda, mp * EB, lds, acc);
 
   const float gamma = (step == 0) ? scales[tr.mat].c : 1.0f;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lh = lane >> 5;
-  const int R0 = tr.bi * kTile + wr * 128, C0 = tr.bj * kTile + wc * 128;
+  const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
+  const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
   float* xm = d.xm;
-
-  if (!last) {
-    T* xs = static_cast<T*>(d.xs);
-    T* xt_out = static_cast<T*>((step & 1) ? d.xt0 : d.xt1);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = C0 + ni * 32 + li;
-          const int row0 = R0 + mi * 32 + 8 * g + 4 * lh;
-          T tv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const long idx = static_cast<long>(row0 + q) * np + col;
-            const float xn = gamma * (1.5f * xm[idx] - 0.5f * acc[mi][ni][4 * g + q]);
-            xm[idx] = xn;
-            tv[q] = from_f32<T>(xn);
-            if constexpr (DT == kBF16) xs[idx] = tv[q];
-          }
-          T* dst = xt_out + static_cast<long>(col) * mp + row0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[q] = tv[q];
-        }
-    return;
-  }
-
-  // last step: U = X_k in the caller's orientation
-  const int m = d.m, n = d.n;
+  T* xs = static_cast<T*>(d.xs);
+  T* xt_out = static_cast<T*>((step & 1) ? d.xt0 : d.xt1);
   const bool trn = d.tr != 0;
-  T* p = static_cast<T*>(d.p);
-  float* upd = d.upd;
   const float step_lr = -lr * d.lr_scale;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = C0 + ni * 32 + li;
-        const int row0 = R0 + mi * 32 + 8 * g + 4 * lh;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = row0 + q;
-          const float u = gamma * (1.5f * xm[static_cast<long>(row) * np + col] - 0.5f * acc[mi][ni][4 * g + q]);
-          // wide (row, col) is caller (row, col), or caller (col, row) when transposed
-          const int orow = trn ? col : row, ocol = trn ? row : col;
-          if (orow < m && ocol < n) {
-            const long o = static_cast<long>(orow) * n + ocol;
-            if (mode == kModeMuon) {
-              p[o] = from_f32<T>(fmaf(step_lr, u, to_f32(p[o])));
-              if (upd) upd[o] = u;
-            } else {
-              p[o] = from_f32<T>(u);
-            }
-          }
-        }
+  __syncthreads();  // operand stages are free
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (wr == h) stage_acc(lds, acc, 1.0f);
+    __syncthreads();
+    // X_new = gamma (1.5 X - 0.5 A X) on rows: chunk tid & 63 of rows (tid >> 6) + 8 k
+#pragma unroll 4
+    for (int k = 0; k < (128 * 64 / kThreads); ++k) {
+      const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
+      const int row = Rt + 128 * h + r, col = Ct + 4 * c;
+      const float4 ax = stage_ld4(lds, r, c);
+      float* xp = xm + static_cast<long>(row) * np + col;
+      const float4 x = *reinterpret_cast<const float4*>(xp);
+      const float xn[4] = {gamma * (1.5f * x.x - 0.5f * ax.x), gamma * (1.5f * x.y - 0.5f * ax.y),
+                           gamma * (1.5f * x.z - 0.5f * ax.z), gamma * (1.5f * x.w - 0.5f * ax.w)};
+      if (!last) {
+        vst4(xp, xn);
+        if constexpr (DT == kBF16) vst4(xs + static_cast<long>(row) * np + col, xn);
+        stage_st4(lds, r, c, make_float4(xn[0], xn[1], xn[2], xn[3]));
+      } else if (!trn) {
+        write_caller<T, 4>(d, mode, step_lr, row, col, xn);
+      } else {
+        stage_st4(lds, r, c, make_float4(xn[0], xn[1], xn[2], xn[3]));
       }
+    }
+    if (!last || trn) {
+      __syncthreads();
+      // transposed outputs: 8-row segments of each column
+#pragma unroll 2
+      for (int j = 0; j < (256 * 16 / kThreads); ++j) {
+        const int q = tid + kThreads * j, sgi = q & 15, col = q >> 4;
+        float v[8];
+        stage_col8(lds, sgi, col, v);
+        const int row0 = Rt + 128 * h + 8 * sgi;
+        if (!last)
+          vst8(xt_out + static_cast<long>(Ct + col) * mp + row0, v);
+        else  // wide (row, col) is caller (col, row)
+          write_caller<T, 8>(d, mode, step_lr, Ct + col, row0, v);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace
