@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", default=True)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device copy of GIB GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -92,6 +94,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * 2**30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
+        return
     cfg = get_config(args.config)
     ns_steps = args.ns_steps if args.ns_steps is not None else cfg.ns_steps[0]
     dt = {"bf16": torch.bfloat16, "f32": torch.float32}[cfg.dtype]
@@ -99,22 +109,9 @@ def main():
     torch.cuda.set_device(dev)
 
     t_setup = time.perf_counter()
-    gen_ = torch.Generator(device=dev)
-    gen_.manual_seed(42)
-    params, grads, moms = [], [], []
-    for spec in cfg.matrices:
-        shape = (spec.rows, spec.cols)
-        g = torch.randn(shape, generator=gen_, device=dev, dtype=torch.float32)
-        if cfg.grad_dist == "student_t3":
-            # t_3 = Z / sqrt(chi2_3 / 3)
-            chi = torch.randn((3,) + shape, generator=gen_, device=dev).pow_(2).sum(0).div_(3.0).sqrt_()
-            g.div_(chi)
-            del chi
-        g.mul_(cfg.grad_scale)
-        grads.append(g.to(dt))
-        del g
-        params.append((torch.randn(shape, generator=gen_, device=dev) * cfg.weight_scale).to(dt))
-        moms.append(torch.zeros(shape, device=dev, dtype=torch.float32))
+    from workloads.device import make_set
+    data = make_set(cfg, device=dev)
+    params, grads, moms = data["params"], data["grads"], data["momentum"]
     step = nsa.MuonStep(params, grads, moms, ns_steps=ns_steps, mu=cfg.momentum, nesterov=cfg.nesterov, lr=cfg.lr)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -192,8 +189,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         import numpy as np
-        # one q_proj (4096x4096) and one k_proj (1024x4096) of layer 0
-        sample = [0, 1] if cfg.key == "llama3_8b" else [0]
+        # layer 0's q_proj (4096x4096), k_proj (1024x4096) and gate_proj (14336x4096): one of each shape
+        sample = [0, 1, 4] if cfg.key == "llama3_8b" else [0]
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, sample, ns_steps, float(np.float32(cfg.momentum)), cfg.lr)
     print(json.dumps(out), flush=True)
