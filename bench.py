@@ -98,7 +98,8 @@ def main():
         n = int(args.copy_calibration * 2**30) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        dst.copy_(src)                      # runtime copy kernel
+        torch.mul(src, 1.0, out=dst)        # elementwise copy kernel
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
         return

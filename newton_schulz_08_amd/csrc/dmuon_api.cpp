@@ -565,7 +565,7 @@ const char* dmuon_backend_info(void) {
   return "dmuon gfx950 | prologue: fused momentum/Nesterov/Frobenius partials, 64x64 LDS-transpose tiles"
          " | syrk: lower-triangle 256x256 tiles + transposed mirror, v_mfma_f32_32x32x16_bf16 / 32x32x2_f32"
          " | ns_gemm: 256x256 tiles, fused 1.5X-0.5AX epilogue, last step writes p -= lr*s*U"
-         " | ragged batch: shape-grouped segments, XCD-contiguous tile order | built " __DATE__;
+         " | ragged batch: shape-grouped segments, per-XCD balanced tile shares | built " __DATE__;
 }
 
 int dmuon_profile_enable(int on) {
