@@ -69,6 +69,26 @@ def cpu_baseline(cfg, sample_idx, ns_steps, mu, lr):
                       f"float64 NumPy oracle"}
 
 
+def reference_gemm(torch, n=8192, reps=30):
+    """Context only: torch.matmul (hipBLASLt) on an n^3 bf16 GEMM of random data on the same GPU, sustained
+    over ~1 s, to show the practical power-limited MFMA rate next to the published peak."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    a = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.matmul(a, b)
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n}, random data (vendor library, context only)",
+            "tflops": 2.0 * n ** 3 / dt / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +98,8 @@ def main():
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", default=True)
+    ap.add_argument("--no-reference-gemm", action="store_true",
+                    help="skip timing the vendor library's bf16 GEMM on the same GPU (context only)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -188,6 +210,8 @@ def main():
         "kernels": kernels,
         "backend": nsa.backend_info(),
     }
+    if not args.no_reference_gemm and cfg.dtype == "bf16":
+        out["reference_gemm"] = reference_gemm(torch)
     if not args.no_cpu_baseline:
         import numpy as np
         # layer 0's q_proj (4096x4096), k_proj (1024x4096) and gate_proj (14336x4096): one of each shape
