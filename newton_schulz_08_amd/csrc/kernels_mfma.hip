@@ -476,43 +476,67 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   const bool trn = d.tr != 0;
   const float step_lr = -lr * d.lr_scale;
   __syncthreads();  // operand stages are free
+  constexpr int kRowIters = 128 * 64 / kThreads;  // 16-byte chunks per thread per half
+  constexpr int kBatch = 4;  // loads in flight ahead of use (register budget: accumulators are live)
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
+    // the iterate rows this thread updates: chunk tid & 63 of rows (tid >> 6) + 8 k.
+    // Loads run kBatch rows ahead of use, the first ones issued before staging and
+    // the barrier, so their latency overlaps the staging and the earlier rows.
+    const int c = tid & 63, col = Ct + 4 * c;
+    auto xrow = [&](int k) { return Rt + 128 * h + (tid >> 6) + (kThreads / 64) * k; };
+    float4 xq[kBatch];  // ring: row k lives in slot k % kBatch
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) xq[k] = *reinterpret_cast<const float4*>(xm + static_cast<long>(xrow(k)) * np + col);
     if (wr == h) stage_acc(lds, acc, 1.0f);
     __syncthreads();
-    // X_new = gamma (1.5 X - 0.5 A X) on rows: chunk tid & 63 of rows (tid >> 6) + 8 k
-#pragma unroll 4
-    for (int k = 0; k < (128 * 64 / kThreads); ++k) {
-      const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
-      const int row = Rt + 128 * h + r, col = Ct + 4 * c;
+    // pass 1, loads only: X_new = gamma (1.5 X - 0.5 A X) replaces A X in the
+    // staging tile.  Each processed row's ring slot is refilled with the load
+    // kBatch rows ahead.  No stores are issued here: vector memory waits count
+    // loads and stores in issue order, so interleaved stores would put their
+    // latency in front of every later load.
+#pragma unroll
+    for (int k = 0; k < kRowIters; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+      const float4 x = xq[k % kBatch];
+      if (k + kBatch < kRowIters)
+        xq[k % kBatch] = *reinterpret_cast<const float4*>(xm + static_cast<long>(xrow(k + kBatch)) * np + col);
+      const int r = (tid >> 6) + (kThreads / 64) * k;
       const float4 ax = stage_ld4(lds, r, c);
-      float* xp = xm + static_cast<long>(row) * np + col;
-      const float4 x = *reinterpret_cast<const float4*>(xp);
-      const float xn[4] = {gamma * (1.5f * x.x - 0.5f * ax.x), gamma * (1.5f * x.y - 0.5f * ax.y),
-                           gamma * (1.5f * x.z - 0.5f * ax.z), gamma * (1.5f * x.w - 0.5f * ax.w)};
-      if (!last) {
-        vst4(xp, xn);
-        if constexpr (DT == kBF16) vst4(xs + static_cast<long>(row) * np + col, xn);
-        stage_st4(lds, r, c, make_float4(xn[0], xn[1], xn[2], xn[3]));
-      } else if (!trn) {
-        write_caller<T, 4>(d, mode, step_lr, row, col, xn);
-      } else {
-        stage_st4(lds, r, c, make_float4(xn[0], xn[1], xn[2], xn[3]));
+      stage_st4(lds, r, c,
+                make_float4(gamma * (1.5f * x.x - 0.5f * ax.x), gamma * (1.5f * x.y - 0.5f * ax.y),
+                            gamma * (1.5f * x.z - 0.5f * ax.z), gamma * (1.5f * x.w - 0.5f * ax.w)));
+    }
+    __syncthreads();
+    // pass 2, stores: rows (iterate and its bf16 copy, or the caller's matrix
+    // when it has the wide orientation) and 8-row column segments (transposed
+    // copy, or the caller's matrix when it is tall)
+    if (!last || !trn) {
+#pragma unroll 4
+      for (int k = 0; k < kRowIters; ++k) {
+        const int r = (tid >> 6) + (kThreads / 64) * k;
+        const int row = Rt + 128 * h + r;
+        const float4 v4 = stage_ld4(lds, r, c);
+        const float xn[4] = {v4.x, v4.y, v4.z, v4.w};
+        if (!last) {
+          vst4(xm + static_cast<long>(row) * np + col, xn);
+          if constexpr (DT == kBF16) vst4(xs + static_cast<long>(row) * np + col, xn);
+        } else {
+          write_caller<T, 4>(d, mode, step_lr, row, col, xn);
+        }
       }
     }
     if (!last || trn) {
-      __syncthreads();
-      // transposed outputs: 8-row segments of each column
 #pragma unroll 2
       for (int j = 0; j < (256 * 16 / kThreads); ++j) {
-        const int q = tid + kThreads * j, sgi = q & 15, col = q >> 4;
+        const int q = tid + kThreads * j, sgi = q & 15, col8 = q >> 4;
         float v[8];
-        stage_col8(lds, sgi, col, v);
+        stage_col8(lds, sgi, col8, v);
         const int row0 = Rt + 128 * h + 8 * sgi;
         if (!last)
-          vst8(xt_out + static_cast<long>(Ct + col) * mp + row0, v);
+          vst8(xt_out + static_cast<long>(Ct + col8) * mp + row0, v);
         else  // wide (row, col) is caller (col, row)
-          write_caller<T, 8>(d, mode, step_lr, Ct + col, row0, v);
+          write_caller<T, 8>(d, mode, step_lr, Ct + col8, row0, v);
       }
     }
     __syncthreads();
