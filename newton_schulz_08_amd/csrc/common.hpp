@@ -77,4 +77,14 @@ struct alignas(16) MatScale {
 
 constexpr int kMaxSegments = 64;
 
+// Memory reached through descriptor fields is device (global) memory.  Saying
+// so makes the compiler emit global_* instead of flat_* accesses: flat ones
+// are counted by the LDS wait counter as well, so with flat stores in flight
+// every wait for an LDS read would also wait for those stores to land.
+template <typename T> using gptr = __attribute__((address_space(1))) T*;
+typedef float f32v4 __attribute__((ext_vector_type(4)));  // builtin vector: copies through gptr
+#if defined(__HIPCC__)
+template <typename T> __device__ __forceinline__ gptr<T> gmem(T* p) { return (gptr<T>)p; }
+#endif
+
 }  // namespace dmuon

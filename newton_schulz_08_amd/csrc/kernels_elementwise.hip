@@ -34,16 +34,16 @@ template <typename T>
 __device__ __forceinline__ void load4(const T* __restrict__ src, bool vec, int valid, float (&v)[4]) {
   if (vec) {
     if constexpr (sizeof(T) == 2) {
-      const bf16x4 x = *reinterpret_cast<const bf16x4*>(src);
+      const bf16x4 x = *reinterpret_cast<gptr<const bf16x4>>(gmem(src));
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = to_f32(x[e]);
     } else {
-      const float4 x = *reinterpret_cast<const float4*>(src);
-      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      const f32v4 x = *reinterpret_cast<gptr<const f32v4>>(gmem(src));
+      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (e < valid) ? to_f32(src[e]) : 0.0f;
+    for (int e = 0; e < 4; ++e) v[e] = (e < valid) ? to_f32(gmem(src)[e]) : 0.0f;
   }
 }
 
@@ -54,14 +54,14 @@ __device__ __forceinline__ void store4(T* __restrict__ dst, bool vec, int valid,
       bf16x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(v[e]);
-      *reinterpret_cast<bf16x4*>(dst) = x;
+      *reinterpret_cast<gptr<bf16x4>>(gmem(dst)) = x;
     } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<gptr<f32v4>>(gmem(dst)) = f32v4{v[0], v[1], v[2], v[3]};
     }
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (e < valid) dst[e] = from_f32<T>(v[e]);
+      if (e < valid) gmem(dst)[e] = from_f32<T>(v[e]);
   }
 }
 

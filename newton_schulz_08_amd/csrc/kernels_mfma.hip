@@ -14,12 +14,17 @@
 // Both are the same "NT" block product C[i,j] = sum_k P[i,k] Q[j,k] with both
 // operands K-contiguous: the Gram uses P = Q = X (rows of X), the update uses
 // P = A and Q = X^T (rows of the transposed iterate, which the previous
-// epilogue keeps up to date).  Each 256-thread workgroup computes a 256x256
-// tile; its four waves own 128x128 quadrants as 4x4 blocks of
-// v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32).  K advances
-// 128 bytes per stage (64 bf16 / 32 fp32) through a double-buffered,
-// XOR-swizzled LDS tile (2 x 64 KB) that global_load_lds fills directly (no
-// register staging) while the current stage is multiplied.
+// epilogue keeps up to date).  Each 512-thread workgroup computes a 256x256
+// tile; its eight waves form a 2 x 4 grid of 128x64 blocks, each 4x2 blocks of
+// v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32), two waves
+// per SIMD.  K advances 128 bytes per stage (64 bf16 / 32 fp32) through a
+// double-buffered, XOR-swizzled LDS tile (2 x 64 KB) that global_load_lds
+// fills directly (no register staging) while the current stage is multiplied;
+// fragment reads and loads are issued one or two at a time between the MFMAs
+// so that no burst of LDS or memory instructions stalls the matrix pipe.
+//
+// All device memory reached through descriptor pointers is accessed with
+// global (not flat) instructions; see gmem().
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -130,6 +135,8 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                : "memory");
 }
 
+template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
 // Wave grid of a 256x256 tile: 2 waves along M (128 rows each) and
 // kWaves / 2 along N; each wave owns kBM x kBN blocks of 32x32.
 template <int kWaves>
@@ -143,17 +150,20 @@ struct WaveGrid {
 
 // Accumulate the 256x256 tile of P * Q^T into acc.  P0/Q0 point at the first
 // row of each 256-row panel; ld*_bytes are row pitches; kbytes the contraction
-// length in bytes (a multiple of 128).
+// length in bytes (a multiple of 128, at least 512).  after_last_barrier() runs
+// once every wave has read its last operand fragment: from then on the
+// caller owns all of the LDS, while the final MFMAs are still in flight.
 //
 // Global -> LDS: global_load_lds_dwordx4 writes lane l's 16 bytes to
 // LDS[M0 + 16 l], so one wave instruction fills 8 rows x 128 bytes.  Each lane
 // fetches the source chunk that belongs in its slot of the XOR-swizzled
 // layout the fragment reads expect, so there is no VGPR staging.  Wave w
 // loads rows [w * 256 / kWaves, (w + 1) * 256 / kWaves) of both operands.
-template <int DT, int kWaves>
+template <int DT, int kWaves, typename AfterLastBarrier>
 __device__ __forceinline__ void block_product(const char* __restrict__ P0, int ldp_bytes,
                                               const char* __restrict__ Q0, int ldq_bytes, int kbytes, char* lds,
-                                              f32x16 (&acc)[4][WaveGrid<kWaves>::kBN]) {
+                                              f32x16 (&acc)[4][WaveGrid<kWaves>::kBN],
+                                              AfterLastBarrier&& after_last_barrier) {
   using G = WaveGrid<kWaves>;
   constexpr int kBN = G::kBN;
   constexpr int kRowsPerWave = 256 / kWaves;
@@ -193,78 +203,98 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
   const int frag_row = li * 128;
   const int sw = (li & 7) ^ ((li >> 3) & 1);
 
-  // Fragments: per sub-step s (16 bf16 / 4x4 fp32 of K) a wave needs 4 row
-  // fragments of P and kBN of Q; two register slots alternate between
-  // sub-steps.  sched_barrier(0) fences pin the software pipeline: the reads
-  // of sub-step s + 1 are issued before the MFMAs of sub-step s, and the
-  // stage barrier sits before the last sub-step's MFMAs so the next stage's
-  // first fragments load while they run.
   using Frag = typename std::conditional<DT == kBF16, bf16x8, f32x4>::type;
   Frag fa[2][4], fb[2][kBN];
-  auto read_frags = [&](int stage, int s, int slot) {
-    const char* sp = lds + stage * kStageBytes + wr * 128 * 128 + frag_row;
-    const char* sq = lds + stage * kStageBytes + kOperandBytes + wc * (kBN * 32) * 128 + frag_row;
+  constexpr int kMfma = 4 * kBN;                    // MFMA blocks per sub-step
+  constexpr int kReads = 4 + kBN;                   // fragment reads per sub-step
+  constexpr int kDma = 2 * G::kLoadsPerOperand;     // DMA loads per stage
+  // read i of a sub-step, in the order the MFMAs need them: fb[0], fa[0], fb[1..], fa[1..]
+  auto read_one = [&](int stage, int s, int rs, int i) {
     const int co = (((2 * s + lh) ^ sw) << 4);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) fa[slot][x] = *reinterpret_cast<const Frag*>(sp + x * 32 * 128 + co);
-#pragma unroll
-    for (int x = 0; x < kBN; ++x) fb[slot][x] = *reinterpret_cast<const Frag*>(sq + x * 32 * 128 + co);
+    const char* base = lds + stage * kStageBytes + frag_row + co;
+    int isb, x;
+    if (i == 0) { isb = 1; x = 0; }
+    else if (i == 1) { isb = 0; x = 0; }
+    else if (i < kBN + 1) { isb = 1; x = i - 1; }
+    else { isb = 0; x = i - kBN; }
+    if (isb) fb[rs][x] = *reinterpret_cast<const Frag*>(base + kOperandBytes + (wc * kBN + x) * 32 * 128);
+    else fa[rs][x] = *reinterpret_cast<const Frag*>(base + (wr * 4 + x) * 32 * 128);
   };
-  auto mfmas = [&](int slot) {
+  auto dma_one = [&](int stage, int kb, int i) {
+    const uint32_t dp = lds_wave + stage * kStageBytes;
+    const int u = i >> 1;
+    if ((i & 1) == 0) lds_dma16(P0, ((u & 1) ? offp1 : offp0) + u * grp_p + kb, dp + u * 1024);
+    else lds_dma16(Q0, ((u & 1) ? offq1 : offq0) + u * grp_q + kb, dp + kOperandBytes + u * 1024);
+  };
+  auto mfma_one = [&](int rs, int j) {
+    const int mi = j / kBN, ni = j % kBN;
     if constexpr (DT == kBF16) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kBN; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][ni], fa[slot][mi], acc[mi][ni], 0, 0, 0);
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[rs][ni], fa[rs][mi], acc[mi][ni], 0, 0, 0);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[rs][ni][e], fa[rs][mi][e], acc[mi][ni], 0, 0, 0);
+    }
+  };
+  // One sub-step: the MFMAs of register slot rs, with the next sub-step's
+  // fragment reads (from (rstage, rsub) into slot rs ^ 1) and DMA loads
+  // d0 .. d0 + nd - 1 of stage dstage spread between them, each group pinned
+  // in place so no burst of LDS or memory issues stalls the MFMA stream.
+  auto substep = [&](int rs, int rstage, int rsub, int dstage, int dkb, int d0, int nd) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+    for (int j = 0; j < kMfma; ++j) {
+      mfma_one(rs, j);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ni = 0; ni < kBN; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[slot][ni][e], fa[slot][mi][e], acc[mi][ni], 0, 0, 0);
+      for (int i = j * kReads / kMfma; i < (j + 1) * kReads / kMfma; ++i) read_one(rstage, rsub, rs ^ 1, i);
+      if (nd > 0) {
+#pragma unroll
+        for (int i = j * (kDma / 2) / kMfma; i < (j + 1) * (kDma / 2) / kMfma; ++i)
+          if (i < nd) dma_one(dstage, dkb, d0 + i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Pipeline: stage kt is multiplied from buffer kt & 1 while stage kt + 1
-  // lands in the other buffer.  Loads for stage kt + 2 are issued right after
-  // the barrier that ends stage kt's fragment reads, into the buffer stage kt
-  // just released, so each load has a full stage to land.  Issuing them there,
-  // after the barrier's full wait, also keeps the LDS-read waits before each
-  // MFMA group partial (the compiler counts the LDS-DMA loads conservatively).
+  // lands in the other buffer.  Stage kt + 2's loads go into buffer kt & 1
+  // once the barrier after sub-step 2 has retired every read of it: half in
+  // sub-step 3 of stage kt, half in sub-step 0 of stage kt + 1.
   const int nk = kbytes / 128;
-  issue(0, 0);
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) dma_one(0, 0, i);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  issue(1, min(1, nk - 1) * 128);
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+  for (int i = 0; i < kDma / 2; ++i) dma_one(1, min(1, nk - 1) * 128, i);
+#pragma unroll
+  for (int i = 0; i < kReads; ++i) read_one(0, 0, 0, i);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt < nk - 1; ++kt) {
     const int c = kt & 1;
-    read_frags(c, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(c, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(c, 3, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
+    substep(0, c, 1, c ^ 1, min(kt + 1, nk - 1) * 128, kDma / 2, kDma / 2);
+    substep(1, c, 2, 0, 0, 0, 0);
+    substep(0, c, 3, 0, 0, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // branch-free: past the end the final stage is re-loaded into the idle
-    // buffer (in bounds, never used) so the loop body stays one basic block
-    issue(c, min(kt + 2, nk - 1) * 128);
-    read_frags(c ^ 1, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+    // past the end the final stage is re-loaded into the idle buffer (in
+    // bounds, never used) so the loop body stays one basic block
+    substep(1, c ^ 1, 0, c, min(kt + 2, nk - 1) * 128, 0, kDma / 2);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // final stage: no more loads; after its barrier nothing reads the operand
+  // buffers again, so the caller may start filling LDS while the last
+  // sub-step's MFMAs run
+  {
+    const int c = (nk - 1) & 1;
+    substep(0, c, 1, 0, 0, 0, 0);
+    substep(1, c, 2, 0, 0, 0, 0);
+    substep(0, c, 3, 0, 0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    after_last_barrier();
+#pragma unroll
+    for (int j = 0; j < kMfma; ++j) mfma_one(1, j);
+  }
 }
 
 #ifndef DMUON_WAVES
@@ -322,22 +352,22 @@ __device__ __forceinline__ void stage_col8(const char* lds, int s, int col, floa
 
 // 4 / 8 consecutive elements of T to and from fp32 (16-byte aligned vectors).
 __device__ __forceinline__ void vst4(float* p, const float* v) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<gptr<f32v4>>(gmem(p)) = f32v4{v[0], v[1], v[2], v[3]};
 }
 __device__ __forceinline__ void vst4(__bf16* p, const float* v) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   bf16x4 x;
 #pragma unroll
   for (int e = 0; e < 4; ++e) x[e] = static_cast<__bf16>(v[e]);
-  *reinterpret_cast<bf16x4*>(p) = x;
+  *reinterpret_cast<gptr<bf16x4>>(gmem(p)) = x;
 }
 __device__ __forceinline__ void vld4(const float* p, float* v) {
-  const float4 x = *reinterpret_cast<const float4*>(p);
-  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  const f32v4 x = *reinterpret_cast<gptr<const f32v4>>(gmem(p));
+  v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
 }
 __device__ __forceinline__ void vld4(const __bf16* p, float* v) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 x = *reinterpret_cast<gptr<const bf16x4>>(gmem(p));
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(x[e]);
 }
@@ -347,7 +377,7 @@ __device__ __forceinline__ void vst8(__bf16* p, const float* v) {
   bf16x8_t x;
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(v[e]);
-  *reinterpret_cast<bf16x8_t*>(p) = x;
+  *reinterpret_cast<gptr<bf16x8_t>>(gmem(p)) = x;
 }
 
 // Last Newton-Schulz step: N consecutive elements of U at caller (orow,
@@ -379,10 +409,10 @@ __device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float s
       for (int e = 0; e < 4; ++e) {
         if (c + e >= d.n) break;
         if (mode == kModeMuon) {
-          p[h4 + e] = static_cast<T>(fmaf(step_lr, u[h4 + e], static_cast<float>(p[h4 + e])));
-          if (upd) upd[h4 + e] = u[h4 + e];
+          gmem(p)[h4 + e] = static_cast<T>(fmaf(step_lr, u[h4 + e], static_cast<float>(gmem(p)[h4 + e])));
+          if (upd) gmem(upd)[h4 + e] = u[h4 + e];
         } else {
-          p[h4 + e] = static_cast<T>(u[h4 + e]);
+          gmem(p)[h4 + e] = static_cast<T>(u[h4 + e]);
         }
       }
     }
@@ -409,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
     for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
   block_product<DT, kWaves>(xs + static_cast<long>(tr.bi) * kTile * ld, ld, xs + static_cast<long>(tr.bj) * kTile * ld,
-                            ld, np * EB, lds, acc);
+                            ld, np * EB, lds, acc, [] {});
 
   const float alpha = first_step ? scales[tr.mat].c2 : 1.0f;
   T* a = static_cast<T*>(d.a);
@@ -464,8 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
 #pragma unroll
     for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
-  block_product<DT, kWaves>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
-                            xt_in + static_cast<long>(tr.bj) * kTile * lda, lda, mp * EB, lds, acc);
+
 
   const float gamma = (step == 0) ? scales[tr.mat].c : 1.0f;
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
@@ -475,71 +504,127 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   T* xt_out = static_cast<T*>((step & 1) ? d.xt0 : d.xt1);
   const bool trn = d.tr != 0;
   const float step_lr = -lr * d.lr_scale;
-  __syncthreads();  // operand stages are free
-  constexpr int kRowIters = 128 * 64 / kThreads;  // 16-byte chunks per thread per half
-  constexpr int kBatch = 4;  // loads in flight ahead of use (register budget: accumulators are live)
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    // the iterate rows this thread updates: chunk tid & 63 of rows (tid >> 6) + 8 k.
-    // Loads run kBatch rows ahead of use, the first ones issued before staging and
-    // the barrier, so their latency overlaps the staging and the earlier rows.
-    const int c = tid & 63, col = Ct + 4 * c;
-    auto xrow = [&](int k) { return Rt + 128 * h + (tid >> 6) + (kThreads / 64) * k; };
-    float4 xq[kBatch];  // ring: row k lives in slot k % kBatch
+  // The tile is finished in four 64-row quarters through two 64 KB LDS
+  // buffers.  Quarter q's fp32 iterate rows arrive by LDS-DMA in the staging
+  // layout, the waves holding its accumulators replace them in place by
+  // gamma (1.5 X - 0.5 A X), and then every wave stores rows and column
+  // segments from LDS.  Quarter q + 1's DMA is issued before quarter q's
+  // stores, so the wait for it (vmcnt counts loads and stores in issue order)
+  // leaves those stores in flight.
+  constexpr int kQRows = 64;
+  constexpr int kQBytes = kQRows * 1024;
+  constexpr int kDmaRows = kQRows / (kThreads / 64);         // rows per wave per quarter
+  constexpr int kRowIt = kQRows * 64 / kThreads;             // row chunks per thread per quarter
+  constexpr int kColIt = 256 * (kQRows / 8) / kThreads;      // column segments per thread per quarter
+  // store instructions per thread per quarter on a non-final step
+  constexpr int kStoresQ = (DT == kBF16) ? (2 * kRowIt + kColIt) : (kRowIt + 2 * kColIt);
+  const int c = tid & 63, col = Ct + 4 * c;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int li = lane & 31, lh = lane >> 5;
+  const int cbase = (wave % Grid::kWN) * kBN * 8;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+  auto dma_quarter = [&](int q) {
+    const char* xb = uniform_ptr(reinterpret_cast<const char*>(xm + static_cast<long>(Rt + kQRows * q) * np + Ct));
+    const uint32_t dst = lds0 + (q & 1) * kQBytes;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) xq[k] = *reinterpret_cast<const float4*>(xm + static_cast<long>(xrow(k)) * np + col);
-    if (wr == h) stage_acc(lds, acc, 1.0f);
-    __syncthreads();
-    // pass 1, loads only: X_new = gamma (1.5 X - 0.5 A X) replaces A X in the
-    // staging tile.  Each processed row's ring slot is refilled with the load
-    // kBatch rows ahead.  No stores are issued here: vector memory waits count
-    // loads and stores in issue order, so interleaved stores would put their
-    // latency in front of every later load.
+    for (int i = 0; i < kDmaRows; ++i) {
+      const int r = wave * kDmaRows + i;
+      const uint32_t voff = static_cast<uint32_t>(r * np * 4 + 16 * (lane ^ ((r ^ (r >> 3)) & 63)));
+      lds_dma16(xb, voff, dst + r * 1024);
+    }
+  };
+  block_product<DT, kWaves>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
+                            xt_in + static_cast<long>(tr.bj) * kTile * lda, lda, mp * EB, lds, acc, [&] {
+    dma_quarter(0);
+    dma_quarter(1);
+  });
+  wait_vmcnt<kDmaRows>();
+  __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kRowIters; ++k) {
-      __builtin_amdgcn_sched_barrier(0);
-      const float4 x = xq[k % kBatch];
-      if (k + kBatch < kRowIters)
-        xq[k % kBatch] = *reinterpret_cast<const float4*>(xm + static_cast<long>(xrow(k + kBatch)) * np + col);
-      const int r = (tid >> 6) + (kThreads / 64) * k;
-      const float4 ax = stage_ld4(lds, r, c);
-      stage_st4(lds, r, c,
-                make_float4(gamma * (1.5f * x.x - 0.5f * ax.x), gamma * (1.5f * x.y - 0.5f * ax.y),
-                            gamma * (1.5f * x.z - 0.5f * ax.z), gamma * (1.5f * x.w - 0.5f * ax.w)));
+  for (int q = 0; q < 4; ++q) {
+    char* buf = lds + (q & 1) * kQBytes;
+    if (wr == (q >> 1)) {
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int mi = 2 * (q & 1) + m2;
+        // all reads of the block row first, then the updates (one LDS round trip)
+        float4 xv[kBN][4];
+#pragma unroll
+        for (int ni = 0; ni < kBN; ++ni)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            xv[ni][g] = *reinterpret_cast<const float4*>(buf + stage_off(32 * m2 + li, cbase + 8 * ni + 2 * g + lh));
+#pragma unroll
+        for (int ni = 0; ni < kBN; ++ni)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 x = xv[ni][g];
+            const f32x16& ax = acc[mi][ni];
+            *reinterpret_cast<float4*>(buf + stage_off(32 * m2 + li, cbase + 8 * ni + 2 * g + lh)) =
+                make_float4(gamma * (1.5f * x.x - 0.5f * ax[4 * g]), gamma * (1.5f * x.y - 0.5f * ax[4 * g + 1]),
+                            gamma * (1.5f * x.z - 0.5f * ax[4 * g + 2]), gamma * (1.5f * x.w - 0.5f * ax[4 * g + 3]));
+          }
+      }
     }
     __syncthreads();
-    // pass 2, stores: rows (iterate and its bf16 copy, or the caller's matrix
-    // when it has the wide orientation) and 8-row column segments (transposed
-    // copy, or the caller's matrix when it is tall)
-    if (!last || !trn) {
-#pragma unroll 4
-      for (int k = 0; k < kRowIters; ++k) {
-        const int r = (tid >> 6) + (kThreads / 64) * k;
-        const int row = Rt + 128 * h + r;
-        const float4 v4 = stage_ld4(lds, r, c);
-        const float xn[4] = {v4.x, v4.y, v4.z, v4.w};
-        if (!last) {
+    if (!last) {
+      // iterate rows (fp32 and its bf16 copy) and 8-row column segments of the
+      // transposed copy, in batches: LDS reads first, then the stores
+#pragma unroll
+      for (int kb = 0; kb < kRowIt; kb += 4) {
+        f32v4 rv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 v4 = stage_ld4(buf, (tid >> 6) + (kThreads / 64) * (kb + k), c);
+          rv[k] = f32v4{v4.x, v4.y, v4.z, v4.w};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int row = Rt + kQRows * q + (tid >> 6) + (kThreads / 64) * (kb + k);
+          const float xn[4] = {rv[k].x, rv[k].y, rv[k].z, rv[k].w};
           vst4(xm + static_cast<long>(row) * np + col, xn);
           if constexpr (DT == kBF16) vst4(xs + static_cast<long>(row) * np + col, xn);
-        } else {
-          write_caller<T, 4>(d, mode, step_lr, row, col, xn);
         }
       }
-    }
-    if (!last || trn) {
-#pragma unroll 2
-      for (int j = 0; j < (256 * 16 / kThreads); ++j) {
-        const int q = tid + kThreads * j, sgi = q & 15, col8 = q >> 4;
+#pragma unroll
+      for (int jb = 0; jb < kColIt; jb += 2) {
+        float cv[2][8];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int qq = tid + kThreads * (jb + j);
+          stage_col8(buf, qq & 7, qq >> 3, cv[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int qq = tid + kThreads * (jb + j);
+          vst8(xt_out + static_cast<long>(Ct + (qq >> 3)) * mp + Rt + kQRows * q + 8 * (qq & 7), cv[j]);
+        }
+      }
+    } else if (!trn) {
+      // final step, wide matrix: caller rows
+#pragma unroll
+      for (int k = 0; k < kRowIt; ++k) {
+        const int r = (tid >> 6) + (kThreads / 64) * k;
+        const float4 v4 = stage_ld4(buf, r, c);
+        const float xn[4] = {v4.x, v4.y, v4.z, v4.w};
+        write_caller<T, 4>(d, mode, step_lr, Rt + kQRows * q + r, col, xn);
+      }
+    } else {
+      // final step, tall matrix: wide (row, col) is caller (col, row)
+#pragma unroll
+      for (int j = 0; j < kColIt; ++j) {
+        const int qq = tid + kThreads * j, sgi = qq & 7, col8 = qq >> 3;
         float v[8];
-        stage_col8(lds, sgi, col8, v);
-        const int row0 = Rt + 128 * h + 8 * sgi;
-        if (!last)
-          vst8(xt_out + static_cast<long>(Ct + col8) * mp + row0, v);
-        else  // wide (row, col) is caller (col, row)
-          write_caller<T, 8>(d, mode, step_lr, Ct + col8, row0, v);
+        stage_col8(buf, sgi, col8, v);
+        write_caller<T, 8>(d, mode, step_lr, Ct + col8, Rt + kQRows * q + 8 * sgi, v);
       }
     }
-    __syncthreads();
+    if (q < 3) {
+      if (!last) wait_vmcnt<kStoresQ>();  // quarter q + 1 landed; q's stores stay in flight
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (q < 2) dma_quarter(q + 2);               // into the buffer quarter q just released
+    }
   }
 }
 
