@@ -69,6 +69,43 @@ def cpu_baseline(cfg, sample_idx, ns_steps, mu, lr):
                       f"float64 NumPy oracle"}
 
 
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None when the
+    MFMA kernel source has changed since the counters were taken (or no summary exists)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "llama3_8b_hbm_counters.md")
+    src = os.path.join(ROOT, "newton_schulz_08_amd", "csrc", "kernels_mfma.hip")
+    try:
+        text = open(path).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    for m in re.finditer(r"traffic (\S+) bytes_per_launch=(\d+) source_sha256=([0-9a-f]{64})", text):
+        if m.group(1) == kernel and m.group(3) == digest:
+            return int(m.group(2))
+    return None
+
+
+def metadata(torch):
+    meta = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "peaks": {"bf16_mfma_tflops": PEAK_TFLOPS["bf16"], "f32_mfma_tflops": PEAK_TFLOPS["f32"],
+                      "hbm_gbs": PEAK_HBM_GBS}}
+    try:
+        meta["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        meta["rocm"] = None
+    try:
+        prop = torch.cuda.get_device_properties(0)
+        meta["gpu"] = prop.name
+        meta["gcn_arch"] = getattr(prop, "gcnArchName", None)
+        meta["cus"] = prop.multi_processor_count
+        meta["max_clock_mhz"] = getattr(prop, "clock_rate", 0) / 1000.0 or None
+    except Exception:  # pragma: no cover
+        pass
+    return meta
+
+
 def reference_gemm(torch, n=8192, reps=30):
     """Context only: torch.matmul (hipBLASLt) on an n^3 bf16 GEMM of random data on the same GPU, sustained
     over ~1 s, to show the practical power-limited MFMA rate next to the published peak."""
@@ -100,6 +137,8 @@ def main():
     ap.add_argument("--profile", action="store_true", default=True)
     ap.add_argument("--no-reference-gemm", action="store_true",
                     help="skip timing the vendor library's bf16 GEMM on the same GPU (context only)")
+    ap.add_argument("--full-gram", action="store_true",
+                    help="ablation: compute every Gram tile instead of the lower triangle plus its mirror")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -109,6 +148,8 @@ def main():
               "matrix set on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
+    if args.full_gram:
+        os.environ["DMUON_NS_KERNEL"] = "gemm"
     import torch
     import newton_schulz_08_amd as nsa
     from workloads import get_config
@@ -149,15 +190,20 @@ def main():
     nsa.profile_read()
     if args.profile:
         nsa.profile_enable(True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i][0].record()
         step()
+        ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     nsa.profile_enable(False)
     kstats = nsa.profile_read() if args.profile else {}
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    import numpy as np
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     shapes = [(m.rows, m.cols) for m in cfg.matrices]
@@ -181,7 +227,8 @@ def main():
         achieved = s["flops"] / (s["total_ms"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": "ns_gemm_kernel<bf16>" if cfg.dtype == "bf16" else
                     "ns_gemm_kernel<f32>", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                    "frac": achieved / peak, "traffic": None,
+                    "frac": achieved / peak, "traffic": recorded_traffic(
+                        "ns_gemm_kernel<bf16>" if cfg.dtype == "bf16" else "ns_gemm_kernel<f32>"),
                     "per_launch_flops": s["flops"] / max(s["launches"], 1),
                     "avg_launch_ms": s["total_ms"] / max(s["launches"], 1)}
     ns_kernel_ms = sum(kstats[k]["total_ms"] for k in ("syrk", "ns_gemm") if k in kstats) / args.steps
@@ -194,6 +241,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms_events": {"median": float(np.median(step_ms)), "min": float(step_ms.min()),
+                           "p90": float(np.percentile(step_ms, 90))},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -203,12 +252,14 @@ def main():
                                f"({', '.join(sorted(set(f'{m.rows}x{m.cols}' for m in cfg.matrices)))}), "
                                f"{cfg.dtype} grads/params, fp32 momentum, ns_steps={ns_steps}, "
                                f"mu={cfg.momentum}, nesterov={cfg.nesterov}, lr={cfg.lr}",
-                   "matrices": cfg.count, "ns_steps": ns_steps, "parallelism": "single-gpu"},
+                   "matrices": cfg.count, "ns_steps": ns_steps, "parallelism": "single-gpu",
+                   "gram": "full (ablation)" if args.full_gram else "lower triangle + mirror"},
         "ns_tflops_kernels": (ns_total / (ns_kernel_ms * 1e-3) / 1e12) if ns_kernel_ms > 0 else None,
         "pct_mfma_peak": 100.0 * value / peak,
         "roofline": roofline,
         "kernels": kernels,
         "backend": nsa.backend_info(),
+        "meta": metadata(torch),
     }
     if not args.no_reference_gemm and cfg.dtype == "bf16":
         out["reference_gemm"] = reference_gemm(torch)

@@ -41,6 +41,11 @@
  *   outputs are unspecified.
  * - Results are bitwise reproducible for the same inputs, and a matrix's result
  *   does not depend on the other matrices in the batch or their order.
+ * - Environment (read at each call): DMUON_NS_KERNEL=gemm computes every tile of
+ *   the Gram matrix X X^T instead of its lower triangle plus a mirrored copy.
+ *   It is a measurement ablation that shows what the triangle saves. Results
+ *   match the default to rounding; every other value, or no value, selects the
+ *   default.
  */
 #ifndef DMUON_H
 #define DMUON_H

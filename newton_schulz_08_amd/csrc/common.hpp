@@ -63,7 +63,7 @@ struct alignas(16) Segment {
   int mat0;           // first entry in the NS descriptor list
   int tm, tn;         // tile grid: rows, cols of 256-tiles (SYRK: tm == tn)
   int kdim;           // contraction length in elements
-  int pad_;
+  int full;           // Gram only: 1 = every tile, no mirror (measurement ablation); 0 = lower triangle
 };
 static_assert(sizeof(Segment) == 32, "Segment layout");
 

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -351,6 +352,10 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     double flops;
   };
   std::vector<SegSpec> syrk_segs, gemm_segs;
+  // DMUON_NS_KERNEL=gemm: compute every Gram tile instead of the lower triangle
+  // plus its mirror, to measure what the triangle saves (same results)
+  const char* gram_env = std::getenv("DMUON_NS_KERNEL");
+  const bool full_gram = gram_env != nullptr && std::strcmp(gram_env, "gemm") == 0;
   for (const Group& g : pl.groups) {
     const int T = static_cast<int>(g.mp / kTile), TN = static_cast<int>(g.np / kTile);
     double sf = 0.0, gf = 0.0;
@@ -362,11 +367,12 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     }
     Segment s{};
     s.mat0 = g.first;
-    s.tiles_per_mat = T * (T + 1) / 2;
+    s.tiles_per_mat = full_gram ? T * T : T * (T + 1) / 2;
     s.ntiles = s.tiles_per_mat * g.count;
     s.tm = T;
     s.tn = T;
     s.kdim = static_cast<int>(g.np);
+    s.full = full_gram ? 1 : 0;
     syrk_segs.push_back(SegSpec{s, sf});
     Segment q{};
     q.mat0 = g.first;

@@ -74,6 +74,7 @@ struct TileRef {
   int bi;    // tile row
   int bj;    // tile col
   int kdim;
+  int full;  // Gram segment computing every tile (no mirror)
 };
 
 __device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lower) {
@@ -85,7 +86,8 @@ __device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lo
   r.mat = sg.mat0 + local / sg.tiles_per_mat;
   const int t = local % sg.tiles_per_mat;
   r.kdim = sg.kdim;
-  if (lower) {
+  r.full = sg.full;
+  if (lower && !sg.full) {
     // t -> (bi, bj), bj <= bi, row-major over the lower triangle
     int bi = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
     while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   T* a = static_cast<T*>(d.a);
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
   const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
-  const bool mirror = tr.bi != tr.bj;
+  const bool mirror = tr.bi != tr.bj && !tr.full;
   __syncthreads();  // operand stages are free
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {

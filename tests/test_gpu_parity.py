@@ -249,6 +249,22 @@ def test_ns_batched_ragged(dtype):
         assert err <= TOL[dtype], (s, err)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_gram_ablation_matches(dtype, monkeypatch):
+    """DMUON_NS_KERNEL=gemm (every Gram tile, no mirror) gives the default
+    path's result to rounding and meets the oracle tolerance."""
+    shapes = [(520, 1030), (1030, 520), (768, 768)]
+    cfg = _adhoc(shapes, dtype, 180 + (dtype == "bf16"))
+    xs = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(len(shapes))]
+    ref = nsa.ns_batched([to_device(x) for x in xs], ns_steps=5)
+    monkeypatch.setenv("DMUON_NS_KERNEL", "gemm")
+    full = nsa.ns_batched([to_device(x) for x in xs], ns_steps=5)
+    torch.cuda.synchronize()
+    for x, r, f, s in zip(xs, ref, full, shapes):
+        assert rel_fro(to_host_f64(f), to_host_f64(r)) <= TOL[dtype] / 10, s
+        assert rel_fro(to_host_f64(f), oracle.newton_schulz(x.as_f64(), 5)) <= TOL[dtype], s
+
+
 def test_ns_batched_in_place():
     x = torch.randn(384, 896, device="cuda")
     ref = nsa.ns_batched([x.clone()], ns_steps=5)[0]
