@@ -20,9 +20,11 @@ other than itself: closed-form spectra, brute-force loops, the SVD polar factor,
 geometric-series momentum, hand-worked fixtures in tests/golden/.
 """
 from .muon import (  # noqa: F401
+    CUBIC,
     EPS,
     MIN_NS_NUMEL,
     apply_update,
+    coefficient_schedule,
     frobenius_norm,
     momentum_update,
     moonlight_lr_scale,

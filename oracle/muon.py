@@ -17,6 +17,14 @@ reason, in the design notes of the repository):
 * Matrices with fewer than 100,000 elements skip Newton-Schulz and use the
   momentum input directly, as the blog's VanillaMuon does for non-matrix
   parameters and as the training guide's predicate excludes them from NS.
+* Custom Newton-Schulz coefficients (the training guide's ``ns_backend`` row:
+  a ``NewtonSchulz(...)`` object "to customise the coefficients", none printed)
+  are read as the odd matrix polynomial that generalises the blog's cubic map:
+  X <- sum_j c_j (X X^T)^j X, with (c0, c1) = (1.5, -0.5) the blog's own map.
+  A schedule may give one coefficient set per step.
+* Weight decay (the training guide's ``weight_decay`` argument, form unstated)
+  is decoupled and uses the unscaled learning rate:
+  p <- p * (1 - lr * wd) - lr * s * U.
 """
 from __future__ import annotations
 
@@ -47,7 +55,31 @@ def frobenius_norm(x: np.ndarray) -> float:
     return float(np.sqrt(np.sum(x * x)))
 
 
-def newton_schulz(g, steps: int) -> np.ndarray:
+# Blog post, "Muon 核心" equation: G_{t+1} = 1.5 G_t - 0.5 G_t G_t^T G_t.
+CUBIC = (1.5, -0.5)
+
+
+def coefficient_schedule(coeffs, steps: int) -> list:
+    """Per-step coefficient tuples: None -> the cubic map at every step; one
+    sequence of numbers -> that polynomial at every step; a sequence of
+    ``steps`` sequences -> one polynomial per step."""
+    if coeffs is None:
+        return [CUBIC] * steps
+    coeffs = list(coeffs)
+    if coeffs and all(np.ndim(c) == 0 for c in coeffs):
+        one = tuple(float(c) for c in coeffs)
+        if len(one) < 2:
+            raise ValueError("a Newton-Schulz polynomial needs at least two coefficients")
+        return [one] * steps
+    if len(coeffs) != steps:
+        raise ValueError(f"a per-step schedule needs {steps} coefficient sets, got {len(coeffs)}")
+    out = [tuple(float(c) for c in row) for row in coeffs]
+    if any(len(row) < 2 for row in out):
+        raise ValueError("a Newton-Schulz polynomial needs at least two coefficients")
+    return out
+
+
+def newton_schulz(g, steps: int, coeffs=None) -> np.ndarray:
     """Cubic Newton-Schulz orthogonalisation.
 
     Blog post, section "Muon 核心：Newton-Schulz 迭代": G0 = G / ||G||_F, then
@@ -63,9 +95,22 @@ def newton_schulz(g, steps: int) -> np.ndarray:
     transposed = rows > cols
     x = g.T if transposed else g
     x = x / (frobenius_norm(x) + EPS)
-    for _ in range(steps):
+    if coeffs is None:
+        for _ in range(steps):
+            a = x @ x.T
+            x = 1.5 * x - 0.5 * (a @ x)
+        return x.T if transposed else x
+    # Custom coefficients (training guide, ``ns_backend`` row): each step maps
+    # X to sum_j c_j A^j X with A = X X^T, the powers formed by repeated
+    # products A (A^(j-1) X).
+    for c in coefficient_schedule(coeffs, steps):
         a = x @ x.T
-        x = 1.5 * x - 0.5 * (a @ x)
+        term = x
+        y = c[0] * x
+        for cj in c[1:]:
+            term = a @ term
+            y = y + cj * term
+        x = y
     return x.T if transposed else x
 
 
@@ -87,19 +132,24 @@ def ns_input(grad, buf_new, mu: float, nesterov: bool) -> np.ndarray:
     return buf_new
 
 
-def muon_direction(y, steps: int) -> np.ndarray:
+def muon_direction(y, steps: int, coeffs=None) -> np.ndarray:
     """Update direction U for one matrix: NS(y), or y itself when the matrix is
     below the NS size threshold (blog VanillaMuon's non-matrix branch applied
     to the training guide's numel < 100,000 exclusion)."""
     y = _f64_2d(y)
     if y.size < MIN_NS_NUMEL:
         return y.copy()
-    return newton_schulz(y, steps)
+    return newton_schulz(y, steps, coeffs)
 
 
-def apply_update(p, u, lr: float, lr_scale: float = 1.0) -> np.ndarray:
-    """p <- p - lr * scale * U (blog VanillaMuon: p.add_(update, alpha=-lr))."""
-    return np.asarray(p, dtype=np.float64) - (lr * lr_scale) * np.asarray(u, dtype=np.float64)
+def apply_update(p, u, lr: float, lr_scale: float = 1.0, weight_decay: float = 0.0) -> np.ndarray:
+    """p <- p - lr * scale * U (blog VanillaMuon: p.add_(update, alpha=-lr)),
+    after the decoupled decay p <- p * (1 - lr * weight_decay) when the
+    training guide's ``weight_decay`` is non-zero."""
+    p = np.asarray(p, dtype=np.float64)
+    if weight_decay != 0.0:
+        p = p * (1.0 - lr * weight_decay)
+    return p - (lr * lr_scale) * np.asarray(u, dtype=np.float64)
 
 
 def moonlight_lr_scale(rows: int, cols: int) -> float:
@@ -110,10 +160,13 @@ def moonlight_lr_scale(rows: int, cols: int) -> float:
 
 def muon_step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], bufs: Sequence[np.ndarray],
               mu: float, nesterov: bool, steps: int, lr: float,
-              lr_scale: Optional[Sequence[float]] = None
+              lr_scale: Optional[Sequence[float]] = None, weight_decay: float = 0.0,
+              moonlight: bool = False, ns_coeffs=None
               ) -> Tuple[list, list, list, list]:
     """One Muon step over a list of matrices, each independent of the others.
 
+    The per-matrix learning-rate multiplier is lr_scale[i] (1 when absent),
+    times 0.2 * sqrt(max(rows, cols)) when ``moonlight`` is set.
     Returns (new_params, new_bufs, updates, norms) where ``updates`` are the U
     matrices (in each parameter's own orientation) and ``norms`` are
     ||ns_input||_F per matrix.
@@ -123,9 +176,11 @@ def muon_step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], bufs: S
         g = _f64_2d(g)
         b_new = momentum_update(b, g, mu)
         y = ns_input(g, b_new, mu, nesterov)
-        u = muon_direction(y, steps)
+        u = muon_direction(y, steps, ns_coeffs)
         s = 1.0 if lr_scale is None else float(lr_scale[i])
-        out_p.append(apply_update(p, u, lr, s))
+        if moonlight:
+            s *= moonlight_lr_scale(*g.shape)
+        out_p.append(apply_update(p, u, lr, s, weight_decay))
         out_b.append(b_new)
         out_u.append(u)
         norms.append(frobenius_norm(y))

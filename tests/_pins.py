@@ -257,6 +257,156 @@ NS_PINS = [
 ]
 
 
+# ----------------------------------------------------------------------------- odd-polynomial NS
+# The training guide lets a NewtonSchulz object replace the blog's cubic map; its
+# coefficients are not printed.  The pins use the classical quintic
+# (15 s - 10 s^3 + 3 s^5) / 8 (rational, so exact arithmetic applies), the
+# widely used quintic (3.4445, -4.7750, 2.0315) and mixed per-step schedules.
+QUINTIC_EXACT = (Fraction(15, 8), Fraction(-5, 4), Fraction(3, 8))
+QUINTIC_FAST = (3.4445, -4.7750, 2.0315)
+
+
+def poly_scalar(s: float, c) -> float:
+    """sum_j c_j s^(2j+1) in plain Python floats."""
+    out, p, s2 = 0.0, s, s * s
+    for cj in c:
+        out += cj * p
+        p *= s2
+    return out
+
+
+def exact_poly_ns(rows, schedule):
+    """Odd-polynomial Newton-Schulz over Fractions with explicit loops:
+    X <- sum_j c_j A^j X with A = X X^T, one coefficient tuple per step."""
+    g = [[Fraction(v) for v in r] for r in rows]
+    m, n = len(g), len(g[0])
+    transposed = m > n
+    if transposed:
+        g = [[g[i][j] for i in range(m)] for j in range(n)]
+        m, n = n, m
+    ss = sum(int(v) * int(v) for r in rows for v in r)
+    scale = Fraction(_isqrt_exact(ss)) + EPS_FRAC
+    x = [[v / scale for v in r] for r in g]
+    for c in schedule:
+        a = [[sum(x[i][t] * x[j][t] for t in range(n)) for j in range(m)] for i in range(m)]
+        term = x
+        y = [[c[0] * v for v in r] for r in x]
+        for cj in c[1:]:
+            term = [[sum(a[i][t] * term[t][j] for t in range(m)) for j in range(n)] for i in range(m)]
+            y = [[y[i][j] + cj * term[i][j] for j in range(n)] for i in range(m)]
+        x = y
+    if transposed:
+        x = [[x[i][j] for i in range(m)] for j in range(n)]
+    return np.array([[float(v) for v in r] for r in x])
+
+
+def pin_poly_exact_rational(ns_poly):
+    schedules = {
+        "quintic x3": [QUINTIC_EXACT] * 3,
+        "mixed": [(Fraction(3, 2), Fraction(-1, 2)), QUINTIC_EXACT, (Fraction(2), Fraction(-3, 2), Fraction(1, 2))],
+        "cubic as a polynomial": [(Fraction(3, 2), Fraction(-1, 2))] * 2,
+    }
+    for case in EXACT_CASES:
+        ss = sum(v * v for r in case for v in r)
+        if math.isqrt(ss) ** 2 != ss:
+            continue
+        for name, sched in schedules.items():
+            want = exact_poly_ns(case, sched)
+            coeffs = [tuple(float(c) for c in row) for row in sched]
+            got = np.asarray(ns_poly(np.array(case, dtype=np.float64), len(sched), coeffs))
+            assert got.shape == want.shape, (case, name)
+            err = rel_fro(got, want)
+            assert err < 1e-14, f"exact polynomial NS mismatch {case} {name}: {err:.3e}"
+
+
+def pin_poly_closed_form_spectrum(ns_poly, shapes=((12, 40), (40, 12), (64, 256)), seed=43):
+    """An odd matrix polynomial keeps singular vectors: each singular value
+    follows the scalar polynomial of its step."""
+    rng = np.random.default_rng(seed)
+    scheds = [[QUINTIC_FAST] * 5, [QUINTIC_FAST] * 3 + [(1.5, -0.5)] * 2,
+              [(1.875, -1.25, 0.375)] * 4, [(2.0, -1.5, 0.5, 0.0)] * 2]
+    for rows, cols in shapes:
+        r = min(rows, cols)
+        sigma = 10.0 ** rng.uniform(-3.0, 0.0, size=r)
+        g, left, right = _spectral_case(rng, rows, cols, sigma)
+        s0 = sigma / (float(np.sqrt(np.sum(sigma * sigma))) + EPS)
+        for sched in scheds:
+            sk = s0.copy()
+            for c in sched:
+                sk = np.array([poly_scalar(float(v), c) for v in sk])
+            want = (left * sk[None, :]) @ right.T
+            got = np.asarray(ns_poly(g, len(sched), sched))
+            err = rel_fro(got, want)
+            assert err < 1e-11, f"polynomial closed form {rows}x{cols} {sched[0]}: {err:.3e}"
+
+
+def _loops_poly_ns(g, schedule):
+    rows = [list(map(float, r)) for r in np.asarray(g)]
+    m, n = len(rows), len(rows[0])
+    transposed = m > n
+    if transposed:
+        rows = [[rows[i][j] for i in range(m)] for j in range(n)]
+        m, n = n, m
+    ss = 0.0
+    for r in rows:
+        for v in r:
+            ss += v * v
+    scale = math.sqrt(ss) + EPS
+    x = [[v / scale for v in r] for r in rows]
+    for c in schedule:
+        a = [[sum(x[i][t] * x[j][t] for t in range(n)) for j in range(m)] for i in range(m)]
+        term = x
+        y = [[c[0] * v for v in r] for r in x]
+        for cj in c[1:]:
+            term = [[sum(a[i][t] * term[t][j] for t in range(m)) for j in range(n)] for i in range(m)]
+            y = [[y[i][j] + cj * term[i][j] for j in range(n)] for i in range(m)]
+        x = y
+    if transposed:
+        x = [[x[i][j] for i in range(m)] for j in range(n)]
+    return np.array(x)
+
+
+def pin_poly_brute_force_loops(ns_poly, shapes=((4, 8), (8, 4), (5, 5)), seed=47):
+    rng = np.random.default_rng(seed)
+    for rows, cols in shapes:
+        g = rng.standard_normal((rows, cols))
+        for sched in ([QUINTIC_FAST] * 5, [(1.5, -0.5), QUINTIC_FAST, (2.0, -1.5, 0.5)]):
+            err = rel_fro(ns_poly(g, len(sched), sched), _loops_poly_ns(g, sched))
+            assert err < 1e-13, (rows, cols, err)
+
+
+def pin_poly_transpose(ns_poly, seed=53):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((20, 52))
+    sched = [QUINTIC_FAST] * 4
+    assert rel_fro(np.asarray(ns_poly(g.T, 4, sched)), np.asarray(ns_poly(g, 4, sched)).T) < 1e-15
+
+
+POLY_PINS = [pin_poly_exact_rational, pin_poly_closed_form_spectrum, pin_poly_brute_force_loops, pin_poly_transpose]
+
+
+# ----------------------------------------------------------------------------- update rule
+def pin_weight_decay(apply_update, fixture):
+    """tests/golden/weight_decay_worked_example.txt bit for bit; a zero update
+    only decays; zero decay is the plain update."""
+    lr, wd, sc = fixture["lr"][0], fixture["wd"][0], fixture["scale"][0]
+    as2 = lambda k: np.array(fixture[k], dtype=np.float64).reshape(2, 2)  # noqa: E731
+    assert np.array_equal(apply_update(as2("p0"), as2("u"), lr, sc, wd), as2("p1"))
+    assert np.array_equal(apply_update(as2("p0"), np.zeros((2, 2)), lr, sc, wd), as2("decayed"))
+    rng = np.random.default_rng(59)
+    p, u = rng.standard_normal((2, 3, 7))
+    assert np.array_equal(apply_update(p, u, 0.02, 1.5, 0.0), p - 0.03 * u)
+
+
+def pin_moonlight_scale(moonlight_lr_scale):
+    """Training guide, hyper-parameter table, ``lr`` row: 0.2 * sqrt(max(m, n))."""
+    assert moonlight_lr_scale(1024, 4096) == 0.2 * 64.0
+    assert moonlight_lr_scale(4096, 1024) == 0.2 * 64.0
+    assert moonlight_lr_scale(4096, 4096) == 0.2 * 64.0
+    assert moonlight_lr_scale(2048, 32) == 0.2 * math.sqrt(2048.0)
+    assert abs(moonlight_lr_scale(14336, 4096) - 0.2 * 119.73303637676612) < 1e-13
+
+
 # ----------------------------------------------------------------------------- momentum / step
 def pin_geometric_series(momentum_update, ns_input, mu=0.95, steps=40, seed=31):
     """Constant gradient g from a zero buffer: B_t = g (1 - mu^t) / (1 - mu);

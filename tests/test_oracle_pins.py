@@ -11,6 +11,42 @@ def test_newton_schulz_pin(pin):
     pin(oracle.newton_schulz)
 
 
+@pytest.mark.parametrize("pin", _pins.POLY_PINS, ids=lambda f: f.__name__)
+def test_polynomial_newton_schulz_pin(pin):
+    pin(oracle.newton_schulz)
+
+
+def test_weight_decay(golden):
+    _pins.pin_weight_decay(oracle.apply_update, golden("weight_decay_worked_example.txt"))
+
+
+def test_moonlight_scale():
+    _pins.pin_moonlight_scale(oracle.moonlight_lr_scale)
+
+
+def test_muon_step_update_options():
+    """Moonlight mode multiplies an explicit lr_scale; weight decay and custom
+    coefficients reach the parameters through apply_update and newton_schulz."""
+    rng = np.random.default_rng(2)
+    p, g = rng.standard_normal((2, 300, 400))
+    b = np.zeros_like(g)
+    coeffs = _pins.QUINTIC_FAST
+    p1, _, u1, _ = oracle.muon_step([p], [g], [b], 0.95, True, 5, 0.02, lr_scale=[1.5], weight_decay=0.1,
+                                    moonlight=True, ns_coeffs=coeffs)
+    y = g + 0.95 * g
+    assert np.array_equal(u1[0], oracle.newton_schulz(y, 5, coeffs))
+    s = 1.5 * oracle.moonlight_lr_scale(300, 400)
+    assert np.array_equal(p1[0], oracle.apply_update(p, u1[0], 0.02, s, 0.1))
+
+
+def test_coefficient_schedule_validation():
+    assert oracle.coefficient_schedule(None, 2) == [oracle.CUBIC, oracle.CUBIC]
+    with pytest.raises(ValueError):
+        oracle.coefficient_schedule([1.0], 3)
+    with pytest.raises(ValueError):
+        oracle.coefficient_schedule([(1.5, -0.5)] * 2, 3)
+
+
 def test_momentum_geometric_series():
     _pins.pin_geometric_series(oracle.momentum_update, oracle.ns_input)
 

@@ -103,3 +103,68 @@ def test_momentum_mutants_are_caught(golden):
     off_by_one_route = lambda y, k: (np.asarray(y) if np.asarray(y).size <= 100_000  # noqa: E731
                                      else oracle.newton_schulz(y, k))
     assert _caught(lambda: _pins.pin_route_threshold(off_by_one_route, oracle.newton_schulz))
+
+
+# ----------------------------------------------------------------------------- odd-polynomial NS
+def _poly_factory(drop_last=False, wrong_power=False, reverse=False, shift=0, gram="xxt"):
+    def ns(g, steps, coeffs):
+        g = np.asarray(g, dtype=np.float64)
+        m, n = g.shape
+        t = m > n
+        x = g.T if t else g
+        x = x / (np.sqrt(float(np.sum(x * x))) + EPS)
+        sched = oracle.coefficient_schedule(coeffs, steps)
+        for k in range(steps):
+            c = list(sched[min(max(k + shift, 0), steps - 1)])
+            if reverse:
+                c = c[::-1]
+            if drop_last and len(c) > 2:
+                c = c[:-1]
+            a = x.T @ x if gram == "xtx" and m == n else x @ x.T
+            if gram == "xtx" and m != n:
+                a = x @ x.T * 1.0000001
+            term, y = x, c[0] * x
+            for j, cj in enumerate(c[1:], start=1):
+                term = (a @ x) if (wrong_power and j > 1) else (a @ term)
+                y = y + cj * term
+            x = y
+        return x.T if t else x
+    return ns
+
+
+POLY_MUTANTS = {
+    "drop_last_term": _poly_factory(drop_last=True),
+    "wrong_power": _poly_factory(wrong_power=True),
+    "reversed_coefficients": _poly_factory(reverse=True),
+    "schedule_shifted": _poly_factory(shift=1),
+    "gram_perturbed": _poly_factory(gram="xtx"),
+}
+
+
+def _fails_some_poly_pin(ns):
+    for pin in _pins.POLY_PINS:
+        try:
+            pin(ns)
+        except (AssertionError, ValueError, np.linalg.LinAlgError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(POLY_MUTANTS))
+def test_polynomial_mutant_is_caught(name):
+    assert _fails_some_poly_pin(POLY_MUTANTS[name]), f"mutant {name} passed every pin"
+
+
+def test_unmutated_polynomial_copy_passes():
+    assert not _fails_some_poly_pin(_poly_factory())
+
+
+def test_update_rule_mutants_are_caught(golden):
+    fixture = golden("weight_decay_worked_example.txt")
+    scaled_decay = lambda p, u, lr, s=1.0, wd=0.0: np.asarray(p) * (1 - lr * s * wd) - lr * s * np.asarray(u)  # noqa: E731
+    decay_after = lambda p, u, lr, s=1.0, wd=0.0: (np.asarray(p) - lr * s * np.asarray(u)) * (1 - lr * wd)  # noqa: E731
+    decay_sign = lambda p, u, lr, s=1.0, wd=0.0: np.asarray(p) * (1 + lr * wd) - lr * s * np.asarray(u)  # noqa: E731
+    for mutant in (scaled_decay, decay_after, decay_sign):
+        assert _caught(lambda: _pins.pin_weight_decay(mutant, fixture))
+    assert _caught(lambda: _pins.pin_moonlight_scale(lambda m, n: 0.2 * np.sqrt(min(m, n))))
+    assert _caught(lambda: _pins.pin_moonlight_scale(lambda m, n: np.sqrt(max(m, n))))
