@@ -12,7 +12,8 @@
  *
  * where NS_k normalises by the Frobenius norm (+1e-7), iterates on the wide
  * orientation (the transpose when rows > cols) and applies k times the cubic
- * map X <- 1.5 X - 0.5 (X X^T) X.
+ * map X <- 1.5 X - 0.5 (X X^T) X, or a custom odd polynomial (dmuon_ns_config).
+ * With weight decay wd the update is p <- p (1 - lr wd) - lr s_i U.
  *
  * Sources: DMuon blog post "DMuon：让矩阵正交化优化器达到接近 AdamW 的分布式训练开销",
  * sections "Muon 核心：Newton-Schulz 迭代" (normalisation, cubic map, transpose
@@ -41,11 +42,11 @@
  *   outputs are unspecified.
  * - Results are bitwise reproducible for the same inputs, and a matrix's result
  *   does not depend on the other matrices in the batch or their order.
- * - Environment (read at each call): DMUON_NS_KERNEL=gemm computes every tile of
- *   the Gram matrix X X^T instead of its lower triangle plus a mirrored copy.
- *   It is a measurement ablation that shows what the triangle saves. Results
- *   match the default to rounding; every other value, or no value, selects the
- *   default.
+ * - Environment (read at each call): DMUON_NS_KERNEL=gemm selects the
+ *   DMUON_NS_DIRECT backend whatever ns_config says: every tile of each Gram
+ *   product instead of its lower triangle plus a mirrored copy.  It is a
+ *   measurement ablation that shows what the triangle saves; results match the
+ *   default to rounding.  Every other value, or no value, changes nothing.
  */
 #ifndef DMUON_H
 #define DMUON_H
@@ -79,11 +80,40 @@ extern "C" {
 #define DMUON_MAX_NS_STEPS 64
 
 /*
- * Workspace size for dmuon_ns_batched over the given shapes, in bytes.
- * Writes *bytes_out and returns DMUON_OK, or an argument error.  Needs no GPU.
+ * Newton-Schulz configuration: the training guide's `ns_backend` ("超参数指南":
+ * "gram" or "direct", or a NewtonSchulz object with custom coefficients; the
+ * pages print no coefficients).  Each step maps the iterate X (wide side) to
+ *
+ *   X <- c0 X + c1 A X + c2 A^2 X,    A = X X^T,
+ *
+ * an odd polynomial in X; (c0, c1) = (1.5, -0.5) with no c2 is the blog's
+ * cubic map ("Muon 核心：Newton-Schulz 迭代").  A NULL config pointer means
+ * { DMUON_NS_GRAM, 0, 0, NULL }.
+ */
+#define DMUON_NS_GRAM 0       /* Gram products on lower-triangle tiles, mirrored (default) */
+#define DMUON_NS_DIRECT 1     /* Gram products on every tile */
+#define DMUON_MAX_NS_TERMS 3  /* c0, c1, c2 */
+typedef struct {
+    int backend;          /* DMUON_NS_GRAM or DMUON_NS_DIRECT */
+    int num_terms;        /* 0: the cubic map (1.5, -0.5); 2 or 3: coefficients from `coeffs` */
+    int per_step;         /* 0: one coefficient set for every step; 1: one set per step (ns_steps sets) */
+    const float* coeffs;  /* host; sets of num_terms floats (c0 first), one after another; read during
+                             the call; every value finite.  Ignored when num_terms is 0. */
+} dmuon_ns_config;
+
+/* Learning-rate scale modes of dmuon_muon_step (s_i below). */
+#define DMUON_LR_SCALE_ONE 0        /* s_i = lr_scale[i], or 1 when lr_scale is NULL */
+#define DMUON_LR_SCALE_MOONLIGHT 1  /* s_i = 0.2 * sqrt(max(rows_i, cols_i)) * (lr_scale[i], or 1) --
+                                       the training guide's per-parameter scaling ("超参数指南", lr) */
+
+/*
+ * Workspace size for dmuon_ns_batched over the given shapes and configuration
+ * (NULL = default), in bytes.  Writes *bytes_out and returns DMUON_OK, or an
+ * argument error.  Needs no GPU.  A three-term polynomial needs an extra
+ * m' x m' buffer per matrix.
  */
 int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
-                             size_t* bytes_out);
+                             const dmuon_ns_config* ns_config, size_t* bytes_out);
 
 /*
  * Newton-Schulz orthogonalisation of `count` independent matrices
@@ -96,19 +126,22 @@ int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols
  * x_out[i] : device, rows[i] x cols[i], `dtype`, written (RNE for bf16).  May
  *            equal x_in[i]; must not overlap any other input or output.
  * ns_steps : 0 .. DMUON_MAX_NS_STEPS; 0 returns the normalised input.
+ * ns_config: NULL (the cubic map, gram backend) or a host configuration, read
+ *            during the call; the workspace must be sized for the same one.
  * Every matrix is orthogonalised, whatever its size.  bf16 inputs run the
  * contractions on bf16 operands with fp32 accumulation and an fp32 iterate.
  */
 int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out,
                      const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
+                     const dmuon_ns_config* ns_config,
                      void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * Workspace size for dmuon_muon_step over the given shapes, in bytes.
- * Needs no GPU.
+ * Workspace size for dmuon_muon_step over the given shapes and Newton-Schulz
+ * configuration (NULL = default), in bytes.  Needs no GPU.
  */
 int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
-                                    size_t* bytes_out);
+                                    const dmuon_ns_config* ns_config, size_t* bytes_out);
 
 /*
  * One Muon step over `count` matrices (blog post VanillaMuon.step with the
@@ -121,9 +154,15 @@ int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_
  * mu            : momentum coefficient (0.95 in the pages' defaults).
  * nesterov      : nonzero -> Y = grad + mu * buf (with the updated buf).
  * ns_steps      : 0 .. DMUON_MAX_NS_STEPS (5 in the pages' defaults).
+ * ns_config     : NULL (cubic map, gram backend) or a host configuration; the
+ *                 workspace must be sized for the same one.
  * lr            : learning rate (0.02 in the pages' defaults).
- * lr_scale      : host array of `count` floats multiplying lr per matrix, or
- *                 NULL for 1.0 (the training guide names 0.2*sqrt(max(m,n))).
+ * weight_decay  : decoupled decay (training guide, creating the optimizer:
+ *                 `weight_decay`, default 0): p <- p (1 - lr wd) - lr s_i U,
+ *                 with the unscaled lr in the decay.  Finite.
+ * lr_scale_mode : DMUON_LR_SCALE_ONE or DMUON_LR_SCALE_MOONLIGHT.
+ * lr_scale      : host array of `count` finite floats multiplying lr per
+ *                 matrix, or NULL for 1.0.
  * update_out    : NULL, or a host array of `count` device pointers (entries
  *                 may be NULL) receiving U_i as float32, rows x cols.
  * norms_out     : NULL, or a device float32 array of `count` entries receiving
@@ -133,7 +172,9 @@ int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_
  */
 int dmuon_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
                     const int64_t* rows, const int64_t* cols, int dtype,
-                    int ns_steps, float mu, int nesterov, float lr, const float* lr_scale,
+                    int ns_steps, const dmuon_ns_config* ns_config,
+                    float mu, int nesterov, float lr, float weight_decay,
+                    int lr_scale_mode, const float* lr_scale,
                     float* const* update_out, float* norms_out,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 

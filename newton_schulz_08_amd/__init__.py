@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     muon_step,
     muon_step_workspace_bytes,
     ns_batched,
+    ns_config,
     ns_workspace_bytes,
     profile_enable,
     profile_read,

@@ -28,6 +28,22 @@ DMUON_MIN_NS_NUMEL = 100000
 DMUON_MAX_DIM = 65536
 DMUON_MAX_NS_STEPS = 64
 
+DMUON_NS_GRAM = 0
+DMUON_NS_DIRECT = 1
+DMUON_MAX_NS_TERMS = 3
+DMUON_LR_SCALE_ONE = 0
+DMUON_LR_SCALE_MOONLIGHT = 1
+
+
+class NsConfig(ctypes.Structure):
+    """dmuon_ns_config."""
+    _fields_ = [
+        ("backend", ctypes.c_int),
+        ("num_terms", ctypes.c_int),
+        ("per_step", ctypes.c_int),
+        ("coeffs", ctypes.POINTER(ctypes.c_float)),
+    ]
+
 
 class KernelStat(ctypes.Structure):
     _fields_ = [
@@ -44,16 +60,17 @@ _PP = ctypes.POINTER(ctypes.c_void_p)
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _SZP = ctypes.POINTER(ctypes.c_size_t)
 _FP = ctypes.POINTER(ctypes.c_float)
+_CFGP = ctypes.POINTER(NsConfig)
 
 # name -> (restype, argtypes); mirrors include/dmuon.h
 SIGNATURES = {
-    "dmuon_ns_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, _I64P, ctypes.c_int, _SZP]),
+    "dmuon_ns_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, _I64P, ctypes.c_int, _CFGP, _SZP]),
     "dmuon_ns_batched": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _I64P, _I64P, ctypes.c_int, ctypes.c_int,
-                                        _P, ctypes.c_size_t, _P]),
-    "dmuon_muon_step_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, _I64P, ctypes.c_int, _SZP]),
+                                        _CFGP, _P, ctypes.c_size_t, _P]),
+    "dmuon_muon_step_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, _I64P, ctypes.c_int, _CFGP, _SZP]),
     "dmuon_muon_step": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _I64P, _I64P, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_float, ctypes.c_int, ctypes.c_float, _FP, _PP, _P,
-                                       _P, ctypes.c_size_t, _P]),
+                                       _CFGP, ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_int, _FP, _PP, _P, _P, ctypes.c_size_t, _P]),
     "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dmuon_last_error": (ctypes.c_char_p, []),
     "dmuon_backend_info": (ctypes.c_char_p, []),

@@ -50,18 +50,66 @@ def _check_matrix(t: torch.Tensor, name: str, dtype: Optional[torch.dtype] = Non
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
-def ns_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtype) -> int:
+_BACKENDS = {"gram": _lib.DMUON_NS_GRAM, "direct": _lib.DMUON_NS_DIRECT}
+
+
+def ns_config(ns_coeffs=None, ns_backend: str = "gram", ns_steps: Optional[int] = None):
+    """A dmuon_ns_config for the given coefficients and backend, or None for the
+    defaults (cubic map, gram backend).
+
+    ns_coeffs: None (the cubic map 1.5, -0.5); one sequence (c0, c1[, c2]) used
+    at every step; or ns_steps such sequences, one per step (two-term sets in a
+    three-term schedule get c2 = 0).
+    ns_backend: "gram" (lower-triangle Gram tiles) or "direct" (every tile).
+    """
+    if ns_backend not in _BACKENDS:
+        raise ValueError(f"ns_backend must be 'gram' or 'direct', got {ns_backend!r}")
+    if ns_coeffs is None and ns_backend == "gram":
+        return None
+    cfg = _lib.NsConfig()
+    cfg.backend = _BACKENDS[ns_backend]
+    if ns_coeffs is None:
+        return cfg
+    rows = list(ns_coeffs)
+    if rows and all(not hasattr(c, "__len__") for c in rows):
+        sets, per_step = [rows], 0
+    else:
+        sets, per_step = [list(r) for r in rows], 1
+        if ns_steps is not None and len(sets) != ns_steps:
+            raise ValueError(f"a per-step schedule needs {ns_steps} coefficient sets, got {len(sets)}")
+    if not sets or any(len(r) not in (2, 3) for r in sets):
+        raise ValueError("each coefficient set must hold 2 or 3 values (c0, c1[, c2])")
+    n = max(len(r) for r in sets)
+    # a two-term set in a three-term schedule is the same map with c2 = 0
+    flat = [float(v) for r in sets for v in (list(r) + [0.0] * (n - len(r)))]
+    arr = (ctypes.c_float * len(flat))(*flat)
+    cfg.num_terms, cfg.per_step = n, per_step
+    cfg.coeffs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    cfg._keep = arr  # the array must outlive the struct
+    return cfg
+
+
+def _cfg_ptr(cfg):
+    return ctypes.byref(cfg) if cfg is not None else None
+
+
+def ns_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtype, ns_coeffs=None,
+                       ns_backend: str = "gram") -> int:
     rows, cols = _shape_arrays(shapes)
     out = ctypes.c_size_t(0)
-    check(_lib.load().dmuon_ns_workspace_bytes(len(shapes), rows, cols, dtype_code(dtype), ctypes.byref(out)),
+    cfg = ns_config(ns_coeffs, ns_backend)
+    check(_lib.load().dmuon_ns_workspace_bytes(len(shapes), rows, cols, dtype_code(dtype), _cfg_ptr(cfg),
+                                               ctypes.byref(out)),
           "dmuon_ns_workspace_bytes")
     return int(out.value)
 
 
-def muon_step_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtype) -> int:
+def muon_step_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtype, ns_coeffs=None,
+                              ns_backend: str = "gram") -> int:
     rows, cols = _shape_arrays(shapes)
     out = ctypes.c_size_t(0)
-    check(_lib.load().dmuon_muon_step_workspace_bytes(len(shapes), rows, cols, dtype_code(dtype),
+    cfg = ns_config(ns_coeffs, ns_backend)
+    check(_lib.load().dmuon_muon_step_workspace_bytes(len(shapes), rows, cols, dtype_code(dtype), _cfg_ptr(cfg),
                                                       ctypes.byref(out)),
           "dmuon_muon_step_workspace_bytes")
     return int(out.value)
@@ -82,8 +130,10 @@ def _stream_handle(stream) -> Optional[int]:
 
 
 def ns_batched(xs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]] = None, ns_steps: int = 5,
-               workspace: Optional[torch.Tensor] = None, stream=None) -> List[torch.Tensor]:
-    """dmuon_ns_batched: out_i = NS_{ns_steps}(x_i) for every matrix."""
+               workspace: Optional[torch.Tensor] = None, stream=None, ns_coeffs=None,
+               ns_backend: str = "gram") -> List[torch.Tensor]:
+    """dmuon_ns_batched: out_i = NS_{ns_steps}(x_i) for every matrix (see
+    ns_config for ns_coeffs and ns_backend)."""
     if len(xs) == 0:
         return []
     dt = xs[0].dtype
@@ -96,12 +146,13 @@ def ns_batched(xs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]
         if o.shape != x.shape:
             raise ValueError(f"outs[{i}] shape {tuple(o.shape)} != {tuple(x.shape)}")
     shapes = [tuple(x.shape) for x in xs]
-    need = ns_workspace_bytes(shapes, dt)
+    cfg = ns_config(ns_coeffs, ns_backend, int(ns_steps))
+    need = ns_workspace_bytes(shapes, dt, ns_coeffs, ns_backend)
     if workspace is None:
         workspace = alloc_workspace(need, xs[0].device)
     rows, cols = _shape_arrays(shapes)
     check(_lib.load().dmuon_ns_batched(len(xs), _ptrs(xs), _ptrs(outs), rows, cols, dtype_code(dt), int(ns_steps),
-                                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                       _cfg_ptr(cfg), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                        ctypes.c_void_p(_stream_handle(stream))),
           "dmuon_ns_batched")
     return list(outs)
@@ -117,7 +168,8 @@ class MuonStep:
 
     def __init__(self, params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                  momentum: Sequence[torch.Tensor], *, ns_steps: int = 5, mu: float = 0.95, nesterov: bool = True,
-                 lr: float = 0.02, lr_scale: Optional[Sequence[float]] = None,
+                 lr: float = 0.02, lr_scale: Optional[Sequence[float]] = None, weight_decay: float = 0.0,
+                 lr_scale_mode: str = "one", ns_coeffs=None, ns_backend: str = "gram",
                  update_out: Optional[Sequence[Optional[torch.Tensor]]] = None,
                  norms_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
         n = len(params)
@@ -155,7 +207,13 @@ class MuonStep:
         self._norms = ctypes.c_void_p(norms_out.data_ptr()) if norms_out is not None else None
         self._scale = (ctypes.c_float * n)(*[float(s) for s in lr_scale]) if lr_scale is not None else None
         self.ns_steps, self.mu, self.nesterov, self.lr = int(ns_steps), float(mu), bool(nesterov), float(lr)
-        self.workspace_bytes = muon_step_workspace_bytes(self.shapes, dt)
+        self.weight_decay = float(weight_decay)
+        modes = {"one": _lib.DMUON_LR_SCALE_ONE, "moonlight": _lib.DMUON_LR_SCALE_MOONLIGHT}
+        if lr_scale_mode not in modes:
+            raise ValueError(f"lr_scale_mode must be 'one' or 'moonlight', got {lr_scale_mode!r}")
+        self._scale_mode = modes[lr_scale_mode]
+        self._cfg = ns_config(ns_coeffs, ns_backend, self.ns_steps)
+        self.workspace_bytes = muon_step_workspace_bytes(self.shapes, dt, ns_coeffs, ns_backend)
         self.workspace = workspace if workspace is not None else alloc_workspace(self.workspace_bytes,
                                                                                  params[0].device)
         if self.workspace.numel() < self.workspace_bytes:
@@ -165,7 +223,8 @@ class MuonStep:
     def __call__(self, stream=None) -> None:
         check(self._lib.dmuon_muon_step(
             self.count, self._params, self._grads, self._mom, self._rows, self._cols, dtype_code(self.dtype),
-            self.ns_steps, ctypes.c_float(self.mu), 1 if self.nesterov else 0, ctypes.c_float(self.lr),
+            self.ns_steps, _cfg_ptr(self._cfg), ctypes.c_float(self.mu), 1 if self.nesterov else 0,
+            ctypes.c_float(self.lr), ctypes.c_float(self.weight_decay), self._scale_mode,
             self._scale, self._upd, self._norms, ctypes.c_void_p(self.workspace.data_ptr()),
             self.workspace.numel(), ctypes.c_void_p(_stream_handle(stream))), "dmuon_muon_step")
 

@@ -29,7 +29,7 @@ enum PrologueMode : int {
   kModeNsOnly = 1, // Y = x (dmuon_ns_batched)
 };
 
-// One matrix of the call.  Lives in the workspace; 128 bytes.
+// One matrix of the call.  Lives in the workspace; 144 bytes.
 struct alignas(16) MatDesc {
   const void* g;     // grad (muon step) or x_in (ns only)
   float* buf;        // momentum buffer (muon step) or nullptr
@@ -40,6 +40,7 @@ struct alignas(16) MatDesc {
   void* xt0;         // workspace: transposed iterate, Np x Mp (even steps)
   void* xt1;         // workspace: transposed iterate, Np x Mp (odd steps)
   void* a;           // workspace: Gram matrix, Mp x Mp
+  void* b;           // workspace: c1 A + c2 A^2 for three-term maps, Mp x Mp (else nullptr)
   int m, n;          // caller shape (rows, cols)
   int mp, np;        // padded wide dims (NS route only)
   int tr;            // 1 when rows > cols (iterate on the transpose)
@@ -51,9 +52,9 @@ struct alignas(16) MatDesc {
   int ew_cols;       // covered extent (cols) for the prologue
   int vec_ok;        // 1 when 4-element vector access is aligned for g/buf/p/upd
   float lr_scale;
-  float pad_[3];
+  float pad_;
 };
-static_assert(sizeof(MatDesc) % 16 == 0, "MatDesc layout");
+static_assert(sizeof(MatDesc) == 144, "MatDesc layout");
 
 // A run of equally shaped Newton-Schulz matrices inside one contraction launch.
 struct alignas(16) Segment {

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -44,8 +45,57 @@ struct MatPlan {
   bool ns, tr;
   int64_t mp, np;     // padded wide dims
   int ew_rows, ew_cols, ew_tiles;
-  size_t off_xm, off_xs, off_xt0, off_xt1, off_a;
+  size_t off_xm, off_xs, off_xt0, off_xt1, off_a, off_b;
 };
+
+// Resolved Newton-Schulz configuration (dmuon_ns_config).
+struct NsCfg {
+  bool direct = false;                        // every Gram tile instead of the lower triangle
+  int terms = 2;                              // 2: c0 X + c1 A X; 3: + c2 A^2 X
+  std::vector<std::array<float, 3>> coeffs;   // one set per step
+};
+
+// Blog post, "Muon 核心" equation: X <- 1.5 X - 0.5 A X.
+constexpr float kCubicC0 = 1.5f, kCubicC1 = -0.5f;
+
+// Validates `cfg`.  With need_coeffs, also reads the coefficients for
+// `ns_steps` steps.  DMUON_NS_KERNEL=gemm forces the direct backend.
+int resolve_ns_config(const dmuon_ns_config* cfg, int ns_steps, bool need_coeffs, NsCfg* out) {
+  NsCfg r;
+  int num_terms = 0, per_step = 0;
+  const float* coeffs = nullptr;
+  if (cfg) {
+    if (cfg->backend != DMUON_NS_GRAM && cfg->backend != DMUON_NS_DIRECT)
+      return fail(DMUON_ERR_INVALID_ARG, "ns_config.backend must be DMUON_NS_GRAM or DMUON_NS_DIRECT");
+    if (cfg->num_terms != 0 && cfg->num_terms != 2 && cfg->num_terms != 3)
+      return fail(DMUON_ERR_INVALID_ARG, "ns_config.num_terms must be 0, 2 or 3");
+    if (cfg->per_step != 0 && cfg->per_step != 1)
+      return fail(DMUON_ERR_INVALID_ARG, "ns_config.per_step must be 0 or 1");
+    r.direct = cfg->backend == DMUON_NS_DIRECT;
+    num_terms = cfg->num_terms;
+    per_step = cfg->per_step;
+    coeffs = cfg->coeffs;
+    if (num_terms != 0 && !coeffs) return fail(DMUON_ERR_INVALID_ARG, "ns_config.coeffs is NULL");
+  }
+  r.terms = num_terms == 3 ? 3 : 2;
+  const char* env = std::getenv("DMUON_NS_KERNEL");
+  if (env != nullptr && std::strcmp(env, "gemm") == 0) r.direct = true;
+  if (need_coeffs) {
+    for (int t = 0; t < ns_steps; ++t) {
+      std::array<float, 3> c{kCubicC0, kCubicC1, 0.0f};
+      if (num_terms != 0) {
+        const float* src = coeffs + (per_step ? t : 0) * num_terms;
+        for (int j = 0; j < num_terms; ++j) {
+          if (!std::isfinite(src[j])) return fail(DMUON_ERR_INVALID_ARG, "ns_config.coeffs must be finite");
+          c[j] = src[j];
+        }
+      }
+      r.coeffs.push_back(c);
+    }
+  }
+  *out = r;
+  return DMUON_OK;
+}
 
 struct Group {
   int64_t mp, np;
@@ -79,8 +129,9 @@ int validate_shapes(int count, const int64_t* rows, const int64_t* cols, int dt)
   return DMUON_OK;
 }
 
-// Build the plan.  `route` = apply the numel < 100000 elementwise route.
-Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool route) {
+// Build the plan.  `route` = apply the numel < 100000 elementwise route;
+// `three_terms` = reserve the m' x m' buffer of a three-term map.
+Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool route, bool three_terms) {
   Plan pl;
   pl.dt = dt;
   pl.count = count;
@@ -154,6 +205,11 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
     off = align_up(off + eb * wide);
     mp.off_a = off;
     off = align_up(off + eb * static_cast<size_t>(mp.mp) * mp.mp);
+    mp.off_b = 0;
+    if (three_terms) {
+      mp.off_b = off;
+      off = align_up(off + eb * static_cast<size_t>(mp.mp) * mp.mp);
+    }
     const double mm = static_cast<double>(std::min(mp.m, mp.n)), nn = static_cast<double>(std::max(mp.m, mp.n));
     pl.syrk_flops += mm * (mm + 1.0) * nn;
     pl.gemm_flops += 2.0 * mm * mm * nn + 3.0 * mm * nn;
@@ -189,8 +245,9 @@ int check_device() {
 }
 
 // ---------------------------------------------------------------- profiler
-enum KernelClass { kKPrologue = 0, kKNorm, kKSyrk, kKGemm, kKApply, kKNumClasses };
-const char* kClassNames[kKNumClasses] = {"prologue", "norm_finalize", "syrk", "ns_gemm", "apply_x0"};
+enum KernelClass { kKPrologue = 0, kKNorm, kKSyrk, kKGemm, kKApply, kKSquare, kKNumClasses };
+const char* kClassNames[kKNumClasses] = {"prologue", "norm_finalize", "syrk", "ns_gemm", "apply_x0",
+                                         "syrk_square"};
 
 struct ProfRecord {
   int cls;
@@ -249,10 +306,13 @@ struct Call {
   void* const* out;          // params or x_out
   float* const* upd;         // update_out (muon, nullable)
   const float* lr_scale;
+  bool moonlight;            // s_i *= 0.2 sqrt(max(rows, cols))
   float* norms_out;
   int ns_steps;
   float mu, lr;
+  float decay;               // 1 - lr * weight_decay
   int nesterov;
+  NsCfg ns;
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -280,6 +340,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
       d.xt0 = ws + mp.off_xt0;
       d.xt1 = ws + mp.off_xt1;
       d.a = ws + mp.off_a;
+      d.b = call.ns.terms == 3 ? ws + mp.off_b : nullptr;
       d.mp = static_cast<int>(mp.mp);
       d.np = static_cast<int>(mp.np);
     }
@@ -297,7 +358,10 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     if (d.buf) vec = vec && aligned(d.buf, 16);
     if (d.upd) vec = vec && aligned(d.upd, 16);
     d.vec_ok = vec ? 1 : 0;
-    d.lr_scale = call.lr_scale ? call.lr_scale[i] : 1.0f;
+    float s = call.lr_scale ? call.lr_scale[i] : 1.0f;
+    // training guide, "超参数指南", lr row: 0.2 * sqrt(max(m, n)) per parameter
+    if (call.moonlight) s *= static_cast<float>(0.2 * std::sqrt(static_cast<double>(std::max(mp.m, mp.n))));
+    d.lr_scale = s;
     prefix[k] = tile0;
     tile0 += mp.ew_tiles;
   }
@@ -328,7 +392,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
   const int ew_grid = std::min(pl.total_tiles, 256 * 8);
   hipError_t e = timed(kKPrologue, 0.0, pro_bytes, stream, [&] {
     return launch_prologue(dt, d_descs, d_prefix, pl.count, pl.total_tiles, d_partials, call.mode, call.mu,
-                           call.nesterov, call.lr, ew_grid, stream);
+                           call.nesterov, call.lr, call.decay, ew_grid, stream);
   });
   if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
   e = timed(kKNorm, 0.0, 4.0 * pl.total_tiles, stream, [&] {
@@ -339,8 +403,8 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
 
   if (call.ns_steps == 0) {
     e = timed(kKApply, 0.0, 0.0, stream, [&] {
-      return launch_apply_x0(dt, d_descs, d_prefix, pl.count, pl.total_tiles, d_scales, call.mode, call.lr, ew_grid,
-                             stream);
+      return launch_apply_x0(dt, d_descs, d_prefix, pl.count, pl.total_tiles, d_scales, call.mode, call.lr,
+                             call.decay, ew_grid, stream);
     });
     if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("apply launch: ") + hipGetErrorString(e));
     return DMUON_OK;
@@ -351,18 +415,18 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     Segment s;
     double flops;
   };
-  std::vector<SegSpec> syrk_segs, gemm_segs;
-  // DMUON_NS_KERNEL=gemm: compute every Gram tile instead of the lower triangle
-  // plus its mirror, to measure what the triangle saves (same results)
-  const char* gram_env = std::getenv("DMUON_NS_KERNEL");
-  const bool full_gram = gram_env != nullptr && std::strcmp(gram_env, "gemm") == 0;
+  std::vector<SegSpec> syrk_segs, square_segs, gemm_segs;
+  // the direct backend (or DMUON_NS_KERNEL=gemm) computes every Gram tile
+  // instead of the lower triangle plus its mirror (same results)
+  const bool full_gram = call.ns.direct;
   for (const Group& g : pl.groups) {
     const int T = static_cast<int>(g.mp / kTile), TN = static_cast<int>(g.np / kTile);
-    double sf = 0.0, gf = 0.0;
+    double sf = 0.0, qf = 0.0, gf = 0.0;
     for (int k = g.first; k < g.first + g.count; ++k) {
       const double mm = static_cast<double>(std::min(pl.mats[k].m, pl.mats[k].n));
       const double nn = static_cast<double>(std::max(pl.mats[k].m, pl.mats[k].n));
       sf += mm * (mm + 1.0) * nn;
+      qf += mm * (mm + 1.0) * mm + 2.0 * mm * mm;
       gf += 2.0 * mm * mm * nn + 3.0 * mm * nn;
     }
     Segment s{};
@@ -374,6 +438,9 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     s.kdim = static_cast<int>(g.np);
     s.full = full_gram ? 1 : 0;
     syrk_segs.push_back(SegSpec{s, sf});
+    Segment sq = s;
+    sq.kdim = static_cast<int>(g.mp);
+    square_segs.push_back(SegSpec{sq, qf});
     Segment q{};
     q.mat0 = g.first;
     q.tiles_per_mat = T * TN;
@@ -385,6 +452,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
   }
   auto by_k = [](const SegSpec& a, const SegSpec& b) { return a.s.kdim > b.s.kdim; };
   std::stable_sort(syrk_segs.begin(), syrk_segs.end(), by_k);
+  std::stable_sort(square_segs.begin(), square_segs.end(), by_k);
   std::stable_sort(gemm_segs.begin(), gemm_segs.end(), by_k);
 
   auto batches = [](const std::vector<SegSpec>& segs) {
@@ -405,19 +473,37 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     return out;
   };
   const auto syrk_launches = batches(syrk_segs);
+  const auto square_launches = batches(square_segs);
   const auto gemm_launches = batches(gemm_segs);
+  const bool three = call.ns.terms == 3;
 
   for (int step = 0; step < call.ns_steps; ++step) {
+    const std::array<float, 3>& c = call.ns.coeffs[step];
     for (const auto& L : syrk_launches) {
       e = timed(kKSyrk, L.second.second, 0.0, stream, [&] {
-        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step == 0 ? 1 : 0, stream);
+        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step == 0 ? 1 : 0, 0, 0.0f, 0.0f,
+                           stream);
       });
       if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk launch: ") + hipGetErrorString(e));
     }
+    // a step whose c2 is zero (a two-term set inside a three-term schedule)
+    // needs no square product
+    const bool sq = three && c[2] != 0.0f;
+    if (sq) {
+      // B = c2 A A + c1 A
+      for (const auto& L : square_launches) {
+        e = timed(kKSquare, L.second.second, 0.0, stream, [&] {
+          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, 0, 1, c[2], c[1], stream);
+        });
+        if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk square launch: ") + hipGetErrorString(e));
+      }
+    }
     const int last = (step + 1 == call.ns_steps) ? 1 : 0;
+    const float cax = sq ? 1.0f : c[1];
     for (const auto& L : gemm_launches) {
       e = timed(kKGemm, L.second.second, 0.0, stream, [&] {
-        return launch_ns_gemm(dt, d_descs, L.first, L.second.first, d_scales, step, last, call.mode, call.lr, stream);
+        return launch_ns_gemm(dt, d_descs, L.first, L.second.first, d_scales, step, last, call.mode, call.lr,
+                              call.decay, c[0], cax, sq ? 1 : 0, stream);
       });
       if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("ns_gemm launch: ") + hipGetErrorString(e));
     }
@@ -461,33 +547,40 @@ using namespace dmuon;
 
 extern "C" {
 
-int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype, size_t* bytes_out) {
+int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                             const dmuon_ns_config* ns_config, size_t* bytes_out) {
   g_last_error.clear();
   if (!bytes_out) return fail(DMUON_ERR_INVALID_ARG, "bytes_out is NULL");
   int st = validate_shapes(count, rows, cols, dtype);
   if (st != DMUON_OK) return st;
-  *bytes_out = count == 0 ? 0 : make_plan(count, rows, cols, dtype, false).total;
+  NsCfg ns;
+  if ((st = resolve_ns_config(ns_config, 0, false, &ns)) != DMUON_OK) return st;
+  *bytes_out = count == 0 ? 0 : make_plan(count, rows, cols, dtype, false, ns.terms == 3).total;
   return DMUON_OK;
 }
 
 int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
-                                    size_t* bytes_out) {
+                                    const dmuon_ns_config* ns_config, size_t* bytes_out) {
   g_last_error.clear();
   if (!bytes_out) return fail(DMUON_ERR_INVALID_ARG, "bytes_out is NULL");
   int st = validate_shapes(count, rows, cols, dtype);
   if (st != DMUON_OK) return st;
-  *bytes_out = count == 0 ? 0 : make_plan(count, rows, cols, dtype, true).total;
+  NsCfg ns;
+  if ((st = resolve_ns_config(ns_config, 0, false, &ns)) != DMUON_OK) return st;
+  *bytes_out = count == 0 ? 0 : make_plan(count, rows, cols, dtype, true, ns.terms == 3).total;
   return DMUON_OK;
 }
 
 int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out, const int64_t* rows,
-                     const int64_t* cols, int dtype, int ns_steps, void* workspace, size_t workspace_bytes,
-                     void* hip_stream) {
+                     const int64_t* cols, int dtype, int ns_steps, const dmuon_ns_config* ns_config,
+                     void* workspace, size_t workspace_bytes, void* hip_stream) {
   g_last_error.clear();
   int st = validate_shapes(count, rows, cols, dtype);
   if (st != DMUON_OK) return st;
   if (ns_steps < 0 || ns_steps > DMUON_MAX_NS_STEPS)
     return fail(DMUON_ERR_INVALID_ARG, "ns_steps outside [0, DMUON_MAX_NS_STEPS]");
+  NsCfg ns;
+  if ((st = resolve_ns_config(ns_config, ns_steps, true, &ns)) != DMUON_OK) return st;
   if (count == 0) return DMUON_OK;
   if ((st = check_ptr_array(count, x_in, "x_in", false)) != DMUON_OK) return st;
   if ((st = check_ptr_array(count, reinterpret_cast<const void* const*>(x_out), "x_out", false)) != DMUON_OK)
@@ -495,7 +588,7 @@ int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out, con
   std::vector<std::pair<const void*, std::string>> outs;
   for (int i = 0; i < count; ++i) outs.push_back({x_out[i], "x_out[" + std::to_string(i) + "]"});
   if ((st = check_distinct(outs)) != DMUON_OK) return st;
-  const Plan pl = make_plan(count, rows, cols, dtype, false);
+  const Plan pl = make_plan(count, rows, cols, dtype, false, ns.terms == 3);
   if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
   if ((st = check_device()) != DMUON_OK) return st;
   Call call{};
@@ -503,19 +596,27 @@ int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out, con
   call.in = x_in;
   call.out = x_out;
   call.ns_steps = ns_steps;
+  call.decay = 1.0f;
+  call.ns = ns;
   return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
 int dmuon_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
-                    const int64_t* rows, const int64_t* cols, int dtype, int ns_steps, float mu, int nesterov,
-                    float lr, const float* lr_scale, float* const* update_out, float* norms_out, void* workspace,
-                    size_t workspace_bytes, void* hip_stream) {
+                    const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
+                    const dmuon_ns_config* ns_config, float mu, int nesterov, float lr, float weight_decay,
+                    int lr_scale_mode, const float* lr_scale, float* const* update_out, float* norms_out,
+                    void* workspace, size_t workspace_bytes, void* hip_stream) {
   g_last_error.clear();
   int st = validate_shapes(count, rows, cols, dtype);
   if (st != DMUON_OK) return st;
   if (ns_steps < 0 || ns_steps > DMUON_MAX_NS_STEPS)
     return fail(DMUON_ERR_INVALID_ARG, "ns_steps outside [0, DMUON_MAX_NS_STEPS]");
-  if (!std::isfinite(mu) || !std::isfinite(lr)) return fail(DMUON_ERR_INVALID_ARG, "mu and lr must be finite");
+  if (!std::isfinite(mu) || !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return fail(DMUON_ERR_INVALID_ARG, "mu, lr and weight_decay must be finite");
+  if (lr_scale_mode != DMUON_LR_SCALE_ONE && lr_scale_mode != DMUON_LR_SCALE_MOONLIGHT)
+    return fail(DMUON_ERR_INVALID_ARG, "lr_scale_mode must be DMUON_LR_SCALE_ONE or DMUON_LR_SCALE_MOONLIGHT");
+  NsCfg ns;
+  if ((st = resolve_ns_config(ns_config, ns_steps, true, &ns)) != DMUON_OK) return st;
   if (count == 0) return DMUON_OK;
   if ((st = check_ptr_array(count, reinterpret_cast<const void* const*>(params), "params", false)) != DMUON_OK)
     return st;
@@ -534,7 +635,7 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
     if (update_out) ptrs.push_back({update_out[i], "update_out" + s});
   }
   if ((st = check_distinct(ptrs)) != DMUON_OK) return st;
-  const Plan pl = make_plan(count, rows, cols, dtype, true);
+  const Plan pl = make_plan(count, rows, cols, dtype, true, ns.terms == 3);
   if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
   if ((st = check_device()) != DMUON_OK) return st;
   Call call{};
@@ -544,11 +645,15 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
   call.out = params;
   call.upd = update_out;
   call.lr_scale = lr_scale;
+  call.moonlight = lr_scale_mode == DMUON_LR_SCALE_MOONLIGHT;
   call.norms_out = norms_out;
   call.ns_steps = ns_steps;
   call.mu = mu;
   call.lr = lr;
+  // decoupled decay with the unscaled lr, formed in double and rounded once
+  call.decay = static_cast<float>(1.0 - static_cast<double>(lr) * static_cast<double>(weight_decay));
   call.nesterov = nesterov ? 1 : 0;
+  call.ns = ns;
   return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
@@ -570,7 +675,8 @@ const char* dmuon_last_error(void) { return g_last_error.c_str(); }
 const char* dmuon_backend_info(void) {
   return "dmuon gfx950 | prologue: fused momentum/Nesterov/Frobenius partials, 64x64 LDS-transpose tiles"
          " | syrk: lower-triangle 256x256 tiles + transposed mirror, v_mfma_f32_32x32x16_bf16 / 32x32x2_f32"
-         " | ns_gemm: 256x256 tiles, fused 1.5X-0.5AX epilogue, last step writes p -= lr*s*U"
+         " | ns_gemm: 256x256 tiles, fused c0 X + c1 A X epilogue (cubic 1.5/-0.5 by default; three-term maps"
+         " add a c2 A^2 + c1 A square launch), last step writes p = p (1 - lr wd) - lr s U"
          " | ragged batch: shape-grouped segments, per-XCD balanced tile shares | built " __DATE__;
 }
 

@@ -5,7 +5,8 @@
 //     Y   <- g + mu * buf  or  buf              (training guide: nesterov ns_input)
 //     partial sum of Y^2 per tile               (Frobenius norm of the NS input)
 //   small matrices (numel < 100000, training guide "编写 Predicate"):
-//     p <- p - lr * s * Y, update_out <- Y      (blog VanillaMuon non-matrix branch)
+//     p <- p (1 - lr wd) - lr * s * Y, update_out <- Y  (blog VanillaMuon non-matrix
+//     branch, with the decoupled weight decay of the training guide's optimizer)
 //   Newton-Schulz matrices: Y is written, unnormalised, as the fp32 iterate, its
 //   operand copy and its transpose in the wide orientation (the transposed
 //   stores go through an LDS tile so both sides stay coalesced).  The 1/||Y||
@@ -84,7 +85,8 @@ template <int DT>
 __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __restrict__ descs,
                                                               const int* __restrict__ prefix, int nmat,
                                                               int total_tiles, float* __restrict__ partials,
-                                                              int mode, float mu, int nesterov, float lr) {
+                                                              int mode, float mu, int nesterov, float lr,
+                                                              float decay) {
   using T = typename Elem<DT>::T;
   __shared__ float tile[kEwTile][kEwTile + 1];
   __shared__ float red[kEwThreads / 64];
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
           T* p = static_cast<T*>(d.p) + o;
           load4(p, vec, valid, pv);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = fmaf(step_lr, y[e], pv[e]);
+          for (int e = 0; e < 4; ++e) pv[e] = fmaf(step_lr, y[e], pv[e] * decay);
           store4(p, vec, valid, pv);
           if (d.upd) store4(d.upd + o, vec, valid, y);
         }
@@ -213,7 +215,7 @@ template <int DT>
 __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __restrict__ descs,
                                                               const int* __restrict__ prefix, int nmat,
                                                               int total_tiles, const MatScale* __restrict__ scales,
-                                                              int mode, float lr) {
+                                                              int mode, float lr, float decay) {
   using T = typename Elem<DT>::T;
   __shared__ float tile[kEwTile][kEwTile + 1];
   const int tid = threadIdx.x;
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
           float pv[4];
           load4(p, vec, valid, pv);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = fmaf(step_lr, u[e], pv[e]);
+          for (int e = 0; e < 4; ++e) pv[e] = fmaf(step_lr, u[e], pv[e] * decay);
           store4(p, vec, valid, pv);
           if (d.upd) store4(d.upd + o, vec, valid, u);
         } else {
@@ -278,15 +280,15 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
 }  // namespace
 
 hipError_t launch_prologue(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
-                           float* partials, int mode, float mu, int nesterov, float lr, int grid,
+                           float* partials, int mode, float mu, int nesterov, float lr, float decay, int grid,
                            hipStream_t stream) {
   if (total_tiles <= 0) return hipSuccess;
   if (dt == kBF16)
     hipLaunchKernelGGL(prologue_kernel<kBF16>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
-                       total_tiles, partials, mode, mu, nesterov, lr);
+                       total_tiles, partials, mode, mu, nesterov, lr, decay);
   else
     hipLaunchKernelGGL(prologue_kernel<kF32>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
-                       total_tiles, partials, mode, mu, nesterov, lr);
+                       total_tiles, partials, mode, mu, nesterov, lr, decay);
   return hipGetLastError();
 }
 
@@ -299,14 +301,14 @@ hipError_t launch_norm_finalize(const MatDesc* descs, const int* tile_prefix, in
 }
 
 hipError_t launch_apply_x0(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
-                           const MatScale* scales, int mode, float lr, int grid, hipStream_t stream) {
+                           const MatScale* scales, int mode, float lr, float decay, int grid, hipStream_t stream) {
   if (total_tiles <= 0) return hipSuccess;
   if (dt == kBF16)
     hipLaunchKernelGGL(apply_x0_kernel<kBF16>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
-                       total_tiles, scales, mode, lr);
+                       total_tiles, scales, mode, lr, decay);
   else
     hipLaunchKernelGGL(apply_x0_kernel<kF32>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
-                       total_tiles, scales, mode, lr);
+                       total_tiles, scales, mode, lr, decay);
   return hipGetLastError();
 }
 

@@ -7,9 +7,15 @@
 //   syrk_kernel    A = alpha * X X^T      lower-triangle 256x256 tiles only; each
 //                                         off-diagonal tile is also stored
 //                                         transposed into the upper triangle.
-//   ns_gemm_kernel X <- g * (1.5 X - 0.5 A X)   fused epilogue; on the last step
+//   ns_gemm_kernel X <- g * (c0 X + c1 A X)    fused epilogue (blog's cubic map:
+//                                         c0 = 1.5, c1 = -0.5); on the last step
 //                                         it writes the update into the caller's
 //                                         parameters (p -= lr * s * X) or output.
+//
+// A three-term map X <- c0 X + c1 A X + c2 A^2 X (custom coefficients, the
+// training guide's NewtonSchulz object) adds one launch per step: syrk_kernel
+// in square mode forms B = c2 A A + c1 A (A symmetric, so A A = A A^T, again
+// on lower-triangle tiles), and ns_gemm_kernel then uses B with c1 = 1.
 //
 // Both are the same "NT" block product C[i,j] = sum_k P[i,k] Q[j,k] with both
 // operands K-contiguous: the Gram uses P = Q = X (rows of X), the update uses
@@ -383,11 +389,12 @@ __device__ __forceinline__ void vst8(__bf16* p, const float* v) {
 }
 
 // Last Newton-Schulz step: N consecutive elements of U at caller (orow,
-// ocol0 ..) -> p -= lr*s*U (+ update_out) or out = U, masked to the caller's
-// shape; 4-element vectors where the row layout and pointers allow it.
+// ocol0 ..) -> p <- p * decay - lr*s*U (+ update_out) or out = U, masked to
+// the caller's shape; 4-element vectors where the row layout and pointers
+// allow it.  decay = 1 - lr * weight_decay (exactly 1 without decay).
 template <typename T, int N>
-__device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float step_lr, int orow, int ocol0,
-                                             const float* u) {
+__device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float step_lr, float decay, int orow,
+                                             int ocol0, const float* u) {
   if (orow >= d.m) return;
   const long o = static_cast<long>(orow) * d.n + ocol0;
   T* p = static_cast<T*>(d.p) + o;
@@ -400,7 +407,7 @@ __device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float s
       if (mode == kModeMuon) {
         vld4(p + h4, v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaf(step_lr, u[h4 + e], v[e]);
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(step_lr, u[h4 + e], v[e] * decay);
         vst4(p + h4, v);
         if (upd) vst4(upd + h4, u + h4);
       } else {
@@ -411,7 +418,7 @@ __device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float s
       for (int e = 0; e < 4; ++e) {
         if (c + e >= d.n) break;
         if (mode == kModeMuon) {
-          gmem(p)[h4 + e] = static_cast<T>(fmaf(step_lr, u[h4 + e], static_cast<float>(gmem(p)[h4 + e])));
+          gmem(p)[h4 + e] = static_cast<T>(fmaf(step_lr, u[h4 + e], static_cast<float>(gmem(p)[h4 + e]) * decay));
           if (upd) gmem(upd)[h4 + e] = u[h4 + e];
         } else {
           gmem(p)[h4 + e] = static_cast<T>(u[h4 + e]);
@@ -423,7 +430,8 @@ __device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float s
 
 template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __restrict__ descs, SegTable st,
-                                                          const MatScale* __restrict__ scales, int first_step) {
+                                                          const MatScale* __restrict__ scales, int first_step,
+                                                          int square, float cq, float cl) {
   using T = typename Elem<DT>::T;
   constexpr int EB = Elem<DT>::kBytes;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
@@ -431,8 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   const TileRef tr = locate(st, blockIdx.x, true);
   const MatDesc& d = descs[tr.mat];
   const int mp = d.mp, np = d.np;
-  const char* xs = static_cast<const char*>(d.xs);
-  const long ld = static_cast<long>(np) * EB;
+  // Gram of the iterate (K = Np), or the square of the symmetric Gram matrix
+  // (K = Mp) for the c2 A^2 term of a three-term map
+  const char* xs = static_cast<const char*>(square ? d.a : d.xs);
+  const int kdim = square ? mp : np;
+  const long ld = static_cast<long>(kdim) * EB;
 
   f32x16 acc[4][kBN];
 #pragma unroll
@@ -441,10 +452,11 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
     for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
   block_product<DT, kWaves>(xs + static_cast<long>(tr.bi) * kTile * ld, ld, xs + static_cast<long>(tr.bj) * kTile * ld,
-                            ld, np * EB, lds, acc, [] {});
+                            ld, kdim * EB, lds, acc, [] {});
 
-  const float alpha = first_step ? scales[tr.mat].c2 : 1.0f;
-  T* a = static_cast<T*>(d.a);
+  const float alpha = square ? cq : (first_step ? scales[tr.mat].c2 : 1.0f);
+  T* a = static_cast<T*>(square ? d.b : d.a);
+  const T* a_in = static_cast<const T*>(d.a);
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
   const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
   const bool mirror = tr.bi != tr.bj && !tr.full;
@@ -453,6 +465,20 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   for (int h = 0; h < 2; ++h) {
     if (wr == h) stage_acc(lds, acc, alpha);
     __syncthreads();
+    if (square) {
+      // B = cq A A + cl A: add cl times this half-tile of A (its own rows; A
+      // is symmetric, so the mirrored copy below stays consistent)
+#pragma unroll 4
+      for (int k = 0; k < (128 * 64 / kThreads); ++k) {
+        const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
+        float av[4];
+        vld4(a_in + static_cast<long>(Rt + 128 * h + r) * mp + Ct + 4 * c, av);
+        const float4 v4 = stage_ld4(lds, r, c);
+        stage_st4(lds, r, c, make_float4(fmaf(cl, av[0], v4.x), fmaf(cl, av[1], v4.y), fmaf(cl, av[2], v4.z),
+                                         fmaf(cl, av[3], v4.w)));
+      }
+      __syncthreads();
+    }
     // A rows: thread covers chunk tid & 63 of rows (tid >> 6) + 8 k
 #pragma unroll 4
     for (int k = 0; k < (128 * 64 / kThreads); ++k) {
@@ -478,7 +504,8 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
 template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __restrict__ descs, SegTable st,
                                                              const MatScale* __restrict__ scales, int step,
-                                                             int last, int mode, float lr) {
+                                                             int last, int mode, float lr, float decay,
+                                                             float cx, float cax, int poly) {
   using T = typename Elem<DT>::T;
   constexpr int EB = Elem<DT>::kBytes;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
@@ -486,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   const TileRef tr = locate(st, blockIdx.x, false);
   const MatDesc& d = descs[tr.mat];
   const int mp = d.mp, np = d.np;
-  const char* a = static_cast<const char*>(d.a);
+  const char* a = static_cast<const char*>(poly ? d.b : d.a);
   const char* xt_in = static_cast<const char*>((step & 1) ? d.xt1 : d.xt0);
   const long lda = static_cast<long>(mp) * EB;
 
@@ -563,8 +590,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
             const float4 x = xv[ni][g];
             const f32x16& ax = acc[mi][ni];
             *reinterpret_cast<float4*>(buf + stage_off(32 * m2 + li, cbase + 8 * ni + 2 * g + lh)) =
-                make_float4(gamma * (1.5f * x.x - 0.5f * ax[4 * g]), gamma * (1.5f * x.y - 0.5f * ax[4 * g + 1]),
-                            gamma * (1.5f * x.z - 0.5f * ax[4 * g + 2]), gamma * (1.5f * x.w - 0.5f * ax[4 * g + 3]));
+                make_float4(gamma * (cx * x.x + cax * ax[4 * g]), gamma * (cx * x.y + cax * ax[4 * g + 1]),
+                            gamma * (cx * x.z + cax * ax[4 * g + 2]), gamma * (cx * x.w + cax * ax[4 * g + 3]));
           }
       }
     }
@@ -609,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
         const int r = (tid >> 6) + (kThreads / 64) * k;
         const float4 v4 = stage_ld4(buf, r, c);
         const float xn[4] = {v4.x, v4.y, v4.z, v4.w};
-        write_caller<T, 4>(d, mode, step_lr, Rt + kQRows * q + r, col, xn);
+        write_caller<T, 4>(d, mode, step_lr, decay, Rt + kQRows * q + r, col, xn);
       }
     } else {
       // final step, tall matrix: wide (row, col) is caller (col, row)
@@ -618,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
         const int qq = tid + kThreads * j, sgi = qq & 7, col8 = qq >> 3;
         float v[8];
         stage_col8(buf, sgi, col8, v);
-        write_caller<T, 8>(d, mode, step_lr, Ct + col8, Rt + kQRows * q + 8 * sgi, v);
+        write_caller<T, 8>(d, mode, step_lr, decay, Ct + col8, Rt + kQRows * q + 8 * sgi, v);
       }
     }
     if (q < 3) {
@@ -633,24 +660,27 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
 }  // namespace
 
 hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                       int first_step, hipStream_t stream) {
+                       int first_step, int square, float cq, float cl, hipStream_t stream) {
   if (ntiles <= 0) return hipSuccess;
   if (dt == kBF16)
-    hipLaunchKernelGGL(syrk_kernel<kBF16>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, first_step);
+    hipLaunchKernelGGL(syrk_kernel<kBF16>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, first_step,
+                       square, cq, cl);
   else
-    hipLaunchKernelGGL(syrk_kernel<kF32>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, first_step);
+    hipLaunchKernelGGL(syrk_kernel<kF32>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, first_step,
+                       square, cq, cl);
   return hipGetLastError();
 }
 
 hipError_t launch_ns_gemm(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                          int step, int last, int mode, float lr, hipStream_t stream) {
+                          int step, int last, int mode, float lr, float decay, float cx, float cax, int poly,
+                          hipStream_t stream) {
   if (ntiles <= 0) return hipSuccess;
   if (dt == kBF16)
     hipLaunchKernelGGL(ns_gemm_kernel<kBF16>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, step, last,
-                       mode, lr);
+                       mode, lr, decay, cx, cax, poly);
   else
     hipLaunchKernelGGL(ns_gemm_kernel<kF32>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, step, last,
-                       mode, lr);
+                       mode, lr, decay, cx, cax, poly);
   return hipGetLastError();
 }
 

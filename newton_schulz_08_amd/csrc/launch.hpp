@@ -18,8 +18,9 @@ struct SegTable {
 
 // Fused momentum / Nesterov / norm partials / small-matrix update / iterate
 // materialisation, over `total_tiles` 64x64 tiles of all matrices.
+// Small-route weight update: p <- p * decay + step_lr * Y with decay = 1 - lr wd.
 hipError_t launch_prologue(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
-                           float* partials, int mode, float mu, int nesterov, float lr, int grid,
+                           float* partials, int mode, float mu, int nesterov, float lr, float decay, int grid,
                            hipStream_t stream);
 
 // Per-matrix sum of the prologue partials -> norm, 1/(norm+eps), squared.
@@ -28,12 +29,19 @@ hipError_t launch_norm_finalize(const MatDesc* descs, const int* tile_prefix, in
 
 // ns_steps == 0: U = X0 = Y / (||Y|| + eps) written to the caller.
 hipError_t launch_apply_x0(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
-                           const MatScale* scales, int mode, float lr, int grid, hipStream_t stream);
+                           const MatScale* scales, int mode, float lr, float decay, int grid, hipStream_t stream);
 
+// Gram products over a launch's segments.
+//   square == 0: A = alpha X X^T (alpha = c^2 at the first step, else 1).
+//   square == 1: B = cq A A + cl A (A symmetric, so A A = A A^T).
 hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                       int first_step, hipStream_t stream);
+                       int first_step, int square, float cq, float cl, hipStream_t stream);
 
+// X <- g (cx X + cax M X) with M = A (poly == 0) or B (poly == 1); g = c at
+// step 0, else 1.  On the last step the result U is written to the caller:
+// p <- p * decay + step_lr * U (mode muon) or out = U (ns only).
 hipError_t launch_ns_gemm(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                          int step, int last, int mode, float lr, hipStream_t stream);
+                          int step, int last, int mode, float lr, float decay, float cx, float cax, int poly,
+                          hipStream_t stream);
 
 }  // namespace dmuon

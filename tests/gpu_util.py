@@ -41,14 +41,28 @@ def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def check_update_faithful(p_new: np.ndarray, p_old: np.ndarray, u_gpu: np.ndarray, lr: float, scale: float,
-                          dtype: str) -> None:
-    """p_new must round p_old - lr*scale*U (with the GPU's own U) to within one
-    ulp of the parameter dtype."""
+                          dtype: str, weight_decay: float = 0.0) -> None:
+    """p_new must round p_old (1 - lr wd) - lr*scale*U (with the GPU's own U)
+    to within one ulp of the parameter dtype.  With decay, the fp32 decay
+    factor and the product p * factor are each rounded once more: 3 * 2^-24 |p|
+    covers both."""
     step = float(np.float32(-np.float32(lr) * np.float32(scale)))
-    exact = p_old + step * u_gpu
+    decay = 1.0 - float(np.float32(lr)) * float(np.float32(weight_decay))
+    exact = p_old * decay + step * u_gpu
     err = np.abs(p_new - exact)
-    bad = err > ulp(exact, dtype) * 1.0000001
-    assert not bad.any(), f"{int(bad.sum())} parameter elements off by more than 1 ulp; max err {err.max():.3e}"
+    bound = ulp(exact, dtype)
+    if weight_decay != 0.0:
+        bound = bound + 3.0 * 2.0 ** -24 * np.abs(p_old)
+    bad = err > bound * 1.0000001
+    assert not bad.any(), f"{int(bad.sum())} parameter elements off by more than the bound; max err {err.max():.3e}"
+
+
+def gpu_lr_scale(scale: float, rows: int, cols: int, moonlight: bool) -> float:
+    """The per-matrix multiplier as the library forms it in fp32."""
+    s = np.float32(scale)
+    if moonlight:
+        s = np.float32(s * np.float32(0.2 * math.sqrt(max(rows, cols))))
+    return float(s)
 
 
 def f32_mu(mu: float) -> float:

@@ -55,13 +55,22 @@ def test_status_strings(lib):
     assert b"gfx950" in lib.dmuon_backend_info()
 
 
-def _ws(lib, shapes, dt=0, fn="dmuon_muon_step_workspace_bytes"):
+def _ws(lib, shapes, dt=0, fn="dmuon_muon_step_workspace_bytes", cfg=None):
     n = len(shapes)
     rows = (ctypes.c_int64 * max(n, 1))(*[s[0] for s in shapes])
     cols = (ctypes.c_int64 * max(n, 1))(*[s[1] for s in shapes])
     out = ctypes.c_size_t(0)
-    st = getattr(lib, fn)(n, rows, cols, dt, ctypes.byref(out))
+    st = getattr(lib, fn)(n, rows, cols, dt, ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(out))
     return st, out.value
+
+
+def _cfg(backend=0, terms=0, per_step=0, coeffs=()):
+    c = _lib.NsConfig()
+    c.backend, c.num_terms, c.per_step = backend, terms, per_step
+    arr = (ctypes.c_float * max(len(coeffs), 1))(*coeffs)
+    c.coeffs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)) if coeffs else None
+    c._keep = arr
+    return c
 
 
 def test_workspace_layout_exact(lib):
@@ -75,6 +84,22 @@ def test_workspace_layout_exact(lib):
     # bf16: fp32 iterate + bf16 operand + 2 bf16 transposed + bf16 Gram
     st, nb16 = _ws(lib, [(512, 2048)], dt=1)
     assert nb16 == 256 + 256 + 1024 + 256 + 512 * 2048 * (4 + 2 + 2 + 2) + 512 * 512 * 2
+    # a three-term polynomial adds the m' x m' buffer B = c1 A + c2 A^2
+    st, nb3 = _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(terms=3, coeffs=(3.4445, -4.775, 2.0315)))
+    assert st == 0 and nb3 == nb16 + 512 * 512 * 2
+    # two terms or another backend need nothing extra
+    assert _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(terms=2, coeffs=(1.5, -0.5)))[1] == nb16
+    assert _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(backend=1))[1] == nb16
+
+
+def test_ns_config_validation(lib):
+    E = _lib
+    for bad in (_cfg(backend=2), _cfg(terms=1, coeffs=(1.0,)), _cfg(terms=4, coeffs=(1, 2, 3, 4)),
+                _cfg(per_step=2), _cfg(terms=2)):
+        assert _ws(lib, [(64, 64)], cfg=bad)[0] == E.DMUON_ERR_INVALID_ARG
+    nan = _cfg(terms=2, coeffs=(1.5, float("nan")))
+    assert _step(lib, cfg=nan) == E.DMUON_ERR_INVALID_ARG
+    assert "finite" in _lib.last_error()
 
 
 def test_workspace_route_and_padding(lib):
@@ -98,11 +123,11 @@ def test_workspace_query_errors(lib):
     assert _ws(lib, [(5, 5)], dt=7)[0] == _lib.DMUON_ERR_UNSUPPORTED_DTYPE
     assert _ws(lib, [])[0] == 0 and _ws(lib, [])[1] == 0
     rows = (ctypes.c_int64 * 1)(4)
-    assert lib.dmuon_muon_step_workspace_bytes(1, rows, rows, 0, None) == _lib.DMUON_ERR_INVALID_ARG
+    assert lib.dmuon_muon_step_workspace_bytes(1, rows, rows, 0, None, None) == _lib.DMUON_ERR_INVALID_ARG
 
 
 def _step(lib, count=1, shapes=((64, 64),), ptrs=None, dt=0, steps=5, mu=0.95, lr=0.02, ws=None, wsb=0,
-          upd=None):
+          upd=None, cfg=None, wd=0.0, mode=0):
     n = len(shapes)
     rows = (ctypes.c_int64 * max(n, 1))(*[s[0] for s in shapes])
     cols = (ctypes.c_int64 * max(n, 1))(*[s[1] for s in shapes])
@@ -112,7 +137,8 @@ def _step(lib, count=1, shapes=((64, 64),), ptrs=None, dt=0, steps=5, mu=0.95, l
                 [base + 0x100000 * (i + 2 * n) for i in range(n)])
     P = lambda v: (ctypes.c_void_p * max(n, 1))(*v)  # noqa: E731
     return lib.dmuon_muon_step(count, P(ptrs[0]), P(ptrs[1]), P(ptrs[2]), rows, cols, dt, steps,
-                               ctypes.c_float(mu), 1, ctypes.c_float(lr), None, upd, None,
+                               ctypes.byref(cfg) if cfg is not None else None, ctypes.c_float(mu), 1,
+                               ctypes.c_float(lr), ctypes.c_float(wd), mode, None, upd, None,
                                ctypes.c_void_p(ws), wsb, None)
 
 
@@ -126,6 +152,10 @@ def test_validation_before_any_device_work(lib):
     assert _step(lib, steps=65) == E.DMUON_ERR_INVALID_ARG
     assert _step(lib, mu=float("nan")) == E.DMUON_ERR_INVALID_ARG
     assert _step(lib, lr=float("inf")) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, wd=float("nan")) == E.DMUON_ERR_INVALID_ARG
+    assert _step(lib, mode=2) == E.DMUON_ERR_INVALID_ARG
+    per_step_short = _cfg(terms=2, per_step=1, coeffs=(1.5, -0.5))   # 1 set read for steps=1 only
+    assert _step(lib, steps=1, cfg=per_step_short, ws=None) == E.DMUON_ERR_WORKSPACE
     assert _step(lib, ptrs=([0], [0x2000], [0x3000])) == E.DMUON_ERR_INVALID_ARG
     assert "params[0] is NULL" in _lib.last_error()
     assert _step(lib, ptrs=([0x1000], [0x1000], [0x3000])) == E.DMUON_ERR_INVALID_ARG
@@ -145,13 +175,16 @@ def test_ns_batched_validation(lib):
     rows = (ctypes.c_int64 * 2)(8, 8)
     P = (ctypes.c_void_p * 2)
     E = _lib
-    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x3000), rows, rows, 0, 5, None, 0, None) == \
-        E.DMUON_ERR_INVALID_ARG
-    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x4000), rows, rows, 0, -2, None, 0, None) == \
-        E.DMUON_ERR_INVALID_ARG
-    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x4000), rows, rows, 0, 5, None, 0, None) == \
-        E.DMUON_ERR_WORKSPACE
-    assert lib.dmuon_ns_batched(0, None, None, None, None, 0, 5, None, 0, None) == E.DMUON_OK
+    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x3000), rows, rows, 0, 5, None, None, 0,
+                                None) == E.DMUON_ERR_INVALID_ARG
+    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x4000), rows, rows, 0, -2, None, None, 0,
+                                None) == E.DMUON_ERR_INVALID_ARG
+    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x4000), rows, rows, 0, 5, None, None, 0,
+                                None) == E.DMUON_ERR_WORKSPACE
+    assert lib.dmuon_ns_batched(0, None, None, None, None, 0, 5, None, None, 0, None) == E.DMUON_OK
+    bad = _cfg(backend=5)
+    assert lib.dmuon_ns_batched(2, P(0x1000, 0x2000), P(0x3000, 0x4000), rows, rows, 0, 5, ctypes.byref(bad),
+                                None, 0, None) == E.DMUON_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path; a GPU is visible")

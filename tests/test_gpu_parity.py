@@ -11,8 +11,8 @@ import newton_schulz_08_amd as nsa
 from workloads import gen
 from workloads.configs import MatrixSpec, SetConfig, get_config
 
-from gpu_util import (TOL, TORCH_DT, check_update_faithful, f32_mu, max_ulp_err_f32, rel_fro, to_device,
-                      to_host_f64, ulp)
+from gpu_util import (TOL, TORCH_DT, check_update_faithful, f32_mu, gpu_lr_scale, max_ulp_err_f32, rel_fro,
+                      to_device, to_host_f64, ulp)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def _adhoc(shapes, dtype, cfg_id, grad_dist="normal", grad_scale=1.0):
 
 
 def run_muon(cfg, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.02, lr_scale=None, nonzero_buf=False,
-             with_update=True):
+             with_update=True, weight_decay=0.0, moonlight=False, ns_coeffs=None, ns_backend="gram"):
     """One dmuon_muon_step over every matrix of cfg; returns host copies."""
     n = cfg.count
     g = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(n)]
@@ -46,7 +46,8 @@ def run_muon(cfg, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.02, lr_scale=None,
         if with_update else None
     norms = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
     nsa.muon_step(dp, dg, db, ns_steps=ns_steps, mu=mu, nesterov=nesterov, lr=lr, lr_scale=lr_scale,
-                  update_out=du, norms_out=norms)
+                  update_out=du, norms_out=norms, weight_decay=weight_decay,
+                  lr_scale_mode="moonlight" if moonlight else "one", ns_coeffs=ns_coeffs, ns_backend=ns_backend)
     torch.cuda.synchronize()
     return dict(
         g=[x.as_f64() for x in g], p0=[x.as_f64() for x in p],
@@ -57,7 +58,7 @@ def run_muon(cfg, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.02, lr_scale=None,
 
 
 def check_against_oracle(cfg, res, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.02, lr_scale=None,
-                         indices=None):
+                         indices=None, weight_decay=0.0, moonlight=False, ns_coeffs=None):
     dtype = cfg.dtype
     mu32 = f32_mu(mu)
     indices = range(cfg.count) if indices is None else indices
@@ -66,7 +67,8 @@ def check_against_oracle(cfg, res, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.0
         spec = cfg.matrices[i]
         s = 1.0 if lr_scale is None else float(lr_scale[i])
         pw, bw, uw, nw = oracle.muon_step([res["p0"][i]], [res["g"][i]], [res["b0"][i]], mu32, nesterov,
-                                          ns_steps, lr, [s])
+                                          ns_steps, lr, [s], weight_decay=weight_decay, moonlight=moonlight,
+                                          ns_coeffs=ns_coeffs)
         # momentum: one fused multiply-add in fp32 -> within one fp32 ulp
         e = max_ulp_err_f32(res["b"][i], bw[0])
         assert e <= 1.0, f"{spec.name}: momentum off by {e:.2f} ulp"
@@ -86,7 +88,8 @@ def check_against_oracle(cfg, res, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.0
                 err = rel_fro(u, uw[0])
                 worst = max(worst, err)
                 assert err <= TOL[dtype], f"{spec.name} {spec.rows}x{spec.cols}: rel err {err:.3e} > {TOL[dtype]}"
-            check_update_faithful(res["p"][i], res["p0"][i], u, lr, s, dtype)
+            check_update_faithful(res["p"][i], res["p0"][i], u, lr, gpu_lr_scale(s, spec.rows, spec.cols, moonlight),
+                                  dtype, weight_decay)
     return worst
 
 
@@ -153,8 +156,8 @@ def test_zero_gradient_gives_zero_update():
 def test_empty_batch_is_noop():
     assert nsa.ns_batched([]) == []
     lib = nsa.load()
-    assert lib.dmuon_muon_step(0, None, None, None, None, None, 0, 5, 0.95, 1, 0.02, None, None, None, None, 0,
-                               None) == 0
+    assert lib.dmuon_muon_step(0, None, None, None, None, None, 0, 5, None, 0.95, 1, 0.02, 0.0, 0, None, None, None,
+                               None, 0, None) == 0
 
 
 def test_route_boundary():
@@ -263,6 +266,52 @@ def test_full_gram_ablation_matches(dtype, monkeypatch):
     for x, r, f, s in zip(xs, ref, full, shapes):
         assert rel_fro(to_host_f64(f), to_host_f64(r)) <= TOL[dtype] / 10, s
         assert rel_fro(to_host_f64(f), oracle.newton_schulz(x.as_f64(), 5)) <= TOL[dtype], s
+
+
+QUINTIC_FAST = (3.4445, -4.7750, 2.0315)
+QUINTIC_CLASSICAL = (1.875, -1.25, 0.375)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_weight_decay_and_moonlight_scale(dtype):
+    """Decoupled decay and the 0.2*sqrt(max(m, n)) multiplier, on both routes."""
+    shapes = [(384, 640), (640, 384), (40, 60), (2048, 32)]
+    cfg = _adhoc(shapes, dtype, 190 + (dtype == "bf16"))
+    scale = [1.0, 0.5, 2.0, 1.5]
+    res = run_muon(cfg, nonzero_buf=True, weight_decay=0.1, lr_scale=scale, moonlight=True)
+    check_against_oracle(cfg, res, weight_decay=0.1, lr_scale=scale, moonlight=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_custom_coefficients_ns_batched(dtype):
+    """Odd-polynomial maps: two- and three-term, fixed and per-step, against the
+    oracle; the direct backend gives the same result as the gram one."""
+    shapes = [(520, 1030), (1030, 520), (256, 768), (300, 700)]
+    cfg = _adhoc(shapes, dtype, 200 + (dtype == "bf16"))
+    xs = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(len(shapes))]
+    dxs = [to_device(x) for x in xs]
+    schedules = [(QUINTIC_FAST, 5), (QUINTIC_CLASSICAL, 5), ([QUINTIC_FAST] * 3 + [(1.5, -0.5)] * 2, 5),
+                 ((1.6, -0.6), 4), ([(2.0, -1.5, 0.5), (1.5, -0.5, 0.0)], 2)]
+    for coeffs, k in schedules:
+        outs = nsa.ns_batched(dxs, ns_steps=k, ns_coeffs=coeffs)
+        torch.cuda.synchronize()
+        for x, o, sh in zip(xs, outs, shapes):
+            err = rel_fro(to_host_f64(o), oracle.newton_schulz(x.as_f64(), k, coeffs))
+            print(f"coeffs {coeffs if not isinstance(coeffs, list) else 'schedule'} k={k} {sh}: {err:.3e}", flush=True)
+            assert err <= TOL[dtype], (coeffs, k, sh, err)
+    gram = nsa.ns_batched(dxs, ns_steps=5, ns_coeffs=QUINTIC_FAST)
+    direct = nsa.ns_batched(dxs, ns_steps=5, ns_coeffs=QUINTIC_FAST, ns_backend="direct")
+    torch.cuda.synchronize()
+    for g_, d_ in zip(gram, direct):
+        assert rel_fro(to_host_f64(d_), to_host_f64(g_)) <= TOL[dtype] / 10
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_muon_step_quintic_with_decay(dtype):
+    shapes = [(600, 1100), (1100, 600), (50, 70)]
+    cfg = _adhoc(shapes, dtype, 210 + (dtype == "bf16"))
+    res = run_muon(cfg, weight_decay=0.05, ns_coeffs=QUINTIC_FAST)
+    check_against_oracle(cfg, res, weight_decay=0.05, ns_coeffs=QUINTIC_FAST)
 
 
 def test_ns_batched_in_place():
