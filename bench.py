@@ -31,13 +31,25 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 
 
-def ns_flops(shapes, ns_steps):
+NS_COEFFS = {
+    "cubic": None,                              # the blog's map (1.5, -0.5)
+    "quintic": (3.4445, -4.7750, 2.0315),       # a widely used fast quintic
+    "classical": (1.875, -1.25, 0.375),         # (15 s - 10 s^3 + 3 s^5) / 8
+}
+
+
+def ns_flops(shapes, ns_steps, three_terms=False):
+    """Algorithmic Newton-Schulz flops per step: the lower-triangle Gram product,
+    for three-term maps the lower-triangle square c2 A A + c1 A, and the
+    update product with its epilogue."""
     syrk = gemm = 0.0
     for r, c in shapes:
         if r * c < 100_000:
             continue
         m, n = float(min(r, c)), float(max(r, c))
         syrk += m * (m + 1.0) * n
+        if three_terms:
+            syrk += m * (m + 1.0) * m + 2.0 * m * m
         gemm += 2.0 * m * m * n + 3.0 * m * n
     return syrk * ns_steps, gemm * ns_steps
 
@@ -137,6 +149,10 @@ def main():
     ap.add_argument("--profile", action="store_true", default=True)
     ap.add_argument("--no-reference-gemm", action="store_true",
                     help="skip timing the vendor library's bf16 GEMM on the same GPU (context only)")
+    ap.add_argument("--ns-coeffs", choices=sorted(NS_COEFFS), default="cubic",
+                    help="Newton-Schulz polynomial (default: the cubic 1.5, -0.5)")
+    ap.add_argument("--weight-decay", type=float, default=0.0)
+    ap.add_argument("--moonlight", action="store_true", help="scale lr by 0.2*sqrt(max(m, n)) per matrix")
     ap.add_argument("--full-gram", action="store_true",
                     help="ablation: compute every Gram tile instead of the lower triangle plus its mirror")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -176,7 +192,10 @@ def main():
     from workloads.device import make_set
     data = make_set(cfg, device=dev)
     params, grads, moms = data["params"], data["grads"], data["momentum"]
-    step = nsa.MuonStep(params, grads, moms, ns_steps=ns_steps, mu=cfg.momentum, nesterov=cfg.nesterov, lr=cfg.lr)
+    coeffs = NS_COEFFS[args.ns_coeffs]
+    step = nsa.MuonStep(params, grads, moms, ns_steps=ns_steps, mu=cfg.momentum, nesterov=cfg.nesterov, lr=cfg.lr,
+                        weight_decay=args.weight_decay, lr_scale_mode="moonlight" if args.moonlight else "one",
+                        ns_coeffs=coeffs)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     print(f"[bench] {cfg.key}: {cfg.count} matrices, workspace {step.workspace_bytes / 2**30:.1f} GiB, "
@@ -207,7 +226,7 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     shapes = [(m.rows, m.cols) for m in cfg.matrices]
-    syrk_f, gemm_f = ns_flops(shapes, ns_steps)
+    syrk_f, gemm_f = ns_flops(shapes, ns_steps, coeffs is not None and len(coeffs) == 3)
     ns_total = syrk_f + gemm_f
     value = ns_total / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
@@ -231,7 +250,7 @@ def main():
                         "ns_gemm_kernel<bf16>" if cfg.dtype == "bf16" else "ns_gemm_kernel<f32>"),
                     "per_launch_flops": s["flops"] / max(s["launches"], 1),
                     "avg_launch_ms": s["total_ms"] / max(s["launches"], 1)}
-    ns_kernel_ms = sum(kstats[k]["total_ms"] for k in ("syrk", "ns_gemm") if k in kstats) / args.steps
+    ns_kernel_ms = sum(kstats[k]["total_ms"] for k in ("syrk", "syrk_square", "ns_gemm") if k in kstats) / args.steps
 
     out = {
         "metric": "Muon step ms + NS TFLOP/s (% of MFMA peak), Llama-8B-shaped matrix set",
@@ -253,7 +272,9 @@ def main():
                                f"{cfg.dtype} grads/params, fp32 momentum, ns_steps={ns_steps}, "
                                f"mu={cfg.momentum}, nesterov={cfg.nesterov}, lr={cfg.lr}",
                    "matrices": cfg.count, "ns_steps": ns_steps, "parallelism": "single-gpu",
-                   "gram": "full (ablation)" if args.full_gram else "lower triangle + mirror"},
+                   "gram": "full (ablation)" if args.full_gram else "lower triangle + mirror",
+                   "ns_coeffs": args.ns_coeffs if coeffs is None else f"{args.ns_coeffs} {coeffs}",
+                   "weight_decay": args.weight_decay, "lr_scale": "moonlight" if args.moonlight else "one"},
         "ns_tflops_kernels": (ns_total / (ns_kernel_ms * 1e-3) / 1e12) if ns_kernel_ms > 0 else None,
         "pct_mfma_peak": 100.0 * value / peak,
         "roofline": roofline,
