@@ -20,10 +20,12 @@ other than itself: closed-form spectra, brute-force loops, the SVD polar factor,
 geometric-series momentum, hand-worked fixtures in tests/golden/.
 """
 from .muon import (  # noqa: F401
+    CLIP_EPS,
     CUBIC,
     EPS,
     MIN_NS_NUMEL,
     apply_update,
+    clip_grad_norm_buckets,
     coefficient_schedule,
     frobenius_norm,
     momentum_update,

@@ -25,6 +25,9 @@ reason, in the design notes of the repository):
 * Weight decay (the training guide's ``weight_decay`` argument, form unstated)
   is decoupled and uses the unscaled learning rate:
   p <- p * (1 - lr * wd) - lr * s * U.
+* Gradient clipping (training guide, "梯度裁剪") follows the global p-norm rule
+  of torch.nn.utils.clip_grad_norm_, which the guide names for the other
+  parameters, applied per segment.
 """
 from __future__ import annotations
 
@@ -185,6 +188,49 @@ def muon_step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], bufs: S
         out_u.append(u)
         norms.append(frobenius_norm(y))
     return out_p, out_b, out_u, norms
+
+
+# Training guide, "梯度裁剪": the Muon-only clip follows the global p-norm rule
+# of torch.nn.utils.clip_grad_norm_ (which the guide uses for the other
+# parameters), with the +1e-6 and the clamp at 1 of that rule.
+CLIP_EPS = 1e-6
+
+
+def clip_grad_norm_buckets(grads: Sequence[np.ndarray], segments: Sequence[int], max_norms: Sequence[float],
+                           norm_type: float = 2.0) -> Tuple[list, list]:
+    """Per-segment global p-norm gradient clipping.
+
+    Training guide, "梯度裁剪": clipping happens before momentum and
+    Newton-Schulz; the fused bucketed form computes each segment's norm, clip
+    coefficient and in-place scaling while "keeping per-segment semantics".
+    Segment s holds the tensors i with segments[i] == s:
+
+        total_s = (sum_{i in s} sum |g_i|^p)^(1/p)   (max |g_i| for p = inf)
+        coef_s  = min(max_norm_s / (total_s + 1e-6), 1)
+        g_i    <- coef_s * g_i
+
+    Returns (clipped grads, per-segment totals).
+    """
+    p = float(norm_type)
+    if not (p > 0.0):
+        raise ValueError("norm_type must be positive (or inf)")
+    gs = [np.asarray(g, dtype=np.float64) for g in grads]
+    nseg = len(max_norms)
+    if any(not 0 <= int(sg) < nseg for sg in segments) or len(segments) != len(gs):
+        raise ValueError("every gradient needs a segment index in [0, len(max_norms))")
+    totals = []
+    for s in range(nseg):
+        members = [g for g, sg in zip(gs, segments) if int(sg) == s]
+        if np.isinf(p):
+            totals.append(max([float(np.max(np.abs(g))) for g in members if g.size] or [0.0]))
+        else:
+            totals.append(float(sum(float(np.sum(np.abs(g) ** p)) for g in members) ** (1.0 / p)))
+    out = []
+    for g, sg in zip(gs, segments):
+        s = int(sg)
+        coef = min(float(max_norms[s]) / (totals[s] + CLIP_EPS), 1.0)
+        out.append(g * coef)
+    return out, totals
 
 
 def orthogonality_error(x) -> float:

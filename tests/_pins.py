@@ -455,3 +455,67 @@ def pin_route_threshold(muon_direction, newton_schulz):
     u = muon_direction(edge, 5)
     assert not np.array_equal(u, edge)
     assert rel_fro(u, newton_schulz(edge, 5)) == 0.0
+
+
+# ----------------------------------------------------------------------------- gradient clipping
+CLIP_EPS = 1e-6
+
+
+def pin_clip_worked_example(clip, fixture):
+    """tests/golden/grad_clip_worked_example.txt (hand-derived, 14 digits)."""
+    mn = fixture["max_norm"]
+    grads = [np.array(fixture["a"]), np.array(fixture["b"]).reshape(1, 2), np.array(fixture["c"])]
+    out, totals = clip(grads, [0, 0, 1], mn)
+    assert np.allclose(totals, fixture["total"], rtol=1e-15, atol=0)
+    for got, key in zip(out, ("a_clipped", "b_clipped", "c_clipped")):
+        assert np.allclose(np.ravel(got), fixture[key], rtol=1e-14, atol=0), key
+    assert np.array_equal(out[2], grads[2]), "a segment under its max_norm must be left exactly unchanged"
+
+
+def pin_clip_closed_forms(clip, seed=61):
+    rng = np.random.default_rng(seed)
+    gs = [rng.standard_normal((7, 9)), rng.standard_normal(13), rng.standard_normal((3, 4, 5))]
+    tot = math.sqrt(sum(float(np.sum(g * g)) for g in gs))
+    # above the threshold the clipped 2-norm is max_norm * total / (total + eps)
+    out, t = clip(gs, [0, 0, 0], [1.0])
+    assert abs(t[0] - tot) < 1e-12 * tot
+    new = math.sqrt(sum(float(np.sum(g * g)) for g in out))
+    assert abs(new - tot / (tot + CLIP_EPS)) < 1e-12
+    # below the threshold nothing changes, bit for bit
+    out, _ = clip(gs, [0, 0, 0], [tot * 2])
+    assert all(np.array_equal(a, b) for a, b in zip(out, gs))
+    # segments are independent; splitting a tensor inside a segment changes nothing
+    out2, t2 = clip(gs, [0, 1, 0], [1.0, 100.0])
+    assert np.array_equal(out2[1], gs[1])
+    flat = np.concatenate([gs[0].ravel(), gs[2].ravel()])
+    outf, tf = clip([flat], [0], [1.0])
+    assert abs(t2[0] - tf[0]) < 1e-12 * tf[0]
+    assert np.allclose(np.concatenate([out2[0].ravel(), out2[2].ravel()]), outf[0], rtol=1e-14, atol=0)
+    # p = 1 is the sum of magnitudes, p = inf the largest magnitude
+    _, t1 = clip(gs, [0, 0, 0], [1.0], norm_type=1.0)
+    assert abs(t1[0] - sum(float(np.sum(np.abs(g))) for g in gs)) < 1e-12 * t1[0]
+    _, ti = clip(gs, [0, 0, 0], [1.0], norm_type=float("inf"))
+    assert ti[0] == max(float(np.max(np.abs(g))) for g in gs)
+
+
+def pin_clip_loops(clip, seed=67):
+    rng = np.random.default_rng(seed)
+    gs = [rng.standard_normal(5) * 3, rng.standard_normal(4), rng.standard_normal(6) * 0.1]
+    seg, mn, p = [0, 1, 0], [1.5, 0.2], 3.0
+    out, tot = clip(gs, seg, mn, norm_type=p)
+    for s in range(2):
+        acc = 0.0
+        for g, sg in zip(gs, seg):
+            if sg == s:
+                for v in g:
+                    acc += abs(float(v)) ** p
+        want = acc ** (1.0 / p)
+        assert abs(tot[s] - want) < 1e-13 * want
+        coef = min(mn[s] / (want + CLIP_EPS), 1.0)
+        for g, o, sg in zip(gs, out, seg):
+            if sg == s:
+                for v, w in zip(g, o):
+                    assert abs(float(w) - float(v) * coef) <= 1e-15 * abs(float(v)) + 1e-300
+
+
+CLIP_PINS = [pin_clip_closed_forms, pin_clip_loops]

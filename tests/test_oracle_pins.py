@@ -47,6 +47,22 @@ def test_coefficient_schedule_validation():
         oracle.coefficient_schedule([(1.5, -0.5)] * 2, 3)
 
 
+def test_grad_clip_worked_example(golden):
+    _pins.pin_clip_worked_example(oracle.clip_grad_norm_buckets, golden("grad_clip_worked_example.txt"))
+
+
+@pytest.mark.parametrize("pin", _pins.CLIP_PINS, ids=lambda f: f.__name__)
+def test_grad_clip_pin(pin):
+    pin(oracle.clip_grad_norm_buckets)
+
+
+def test_grad_clip_rejects_bad_segments():
+    with pytest.raises(ValueError):
+        oracle.clip_grad_norm_buckets([np.ones(3)], [1], [1.0])
+    with pytest.raises(ValueError):
+        oracle.clip_grad_norm_buckets([np.ones(3)], [0], [1.0], norm_type=0.0)
+
+
 def test_momentum_geometric_series():
     _pins.pin_geometric_series(oracle.momentum_update, oracle.ns_input)
 

@@ -168,3 +168,50 @@ def test_update_rule_mutants_are_caught(golden):
         assert _caught(lambda: _pins.pin_weight_decay(mutant, fixture))
     assert _caught(lambda: _pins.pin_moonlight_scale(lambda m, n: 0.2 * np.sqrt(min(m, n))))
     assert _caught(lambda: _pins.pin_moonlight_scale(lambda m, n: np.sqrt(max(m, n))))
+
+
+# ----------------------------------------------------------------------------- gradient clipping
+def _clip_factory(eps_outside=False, no_clamp=False, per_tensor=False, no_root=False, one_segment=False):
+    def clip(grads, segments, max_norms, norm_type=2.0):
+        gs = [np.asarray(g, dtype=np.float64) for g in grads]
+        seg = [0] * len(gs) if one_segment else list(segments)
+        p = float(norm_type)
+        def norm(members):
+            if np.isinf(p):
+                return max(float(np.max(np.abs(g))) for g in members)
+            acc = sum(float(np.sum(np.abs(g) ** p)) for g in members)
+            return acc if no_root else acc ** (1.0 / p)
+        totals = [norm([g for g, sg in zip(gs, seg) if sg == s] or [np.zeros(1)]) for s in range(len(max_norms))]
+        out = []
+        for g, sg in zip(gs, seg):
+            t = norm([g]) if per_tensor else totals[sg]
+            coef = max_norms[sg] / t + 1e-6 if eps_outside else max_norms[sg] / (t + 1e-6)
+            out.append(g * (coef if no_clamp else min(coef, 1.0)))
+        return out, totals
+    return clip
+
+
+CLIP_MUTANTS = {
+    "eps_outside": _clip_factory(eps_outside=True),
+    "no_clamp": _clip_factory(no_clamp=True),
+    "per_tensor_norm": _clip_factory(per_tensor=True),
+    "no_root": _clip_factory(no_root=True),
+    "one_segment": _clip_factory(one_segment=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CLIP_MUTANTS))
+def test_clip_mutant_is_caught(name, golden):
+    fixture = golden("grad_clip_worked_example.txt")
+    mutant = CLIP_MUTANTS[name]
+    caught = _caught(lambda: _pins.pin_clip_worked_example(mutant, fixture))
+    for pin in _pins.CLIP_PINS:
+        caught = caught or _caught(lambda: pin(mutant))
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_clip_copy_passes(golden):
+    fixture = golden("grad_clip_worked_example.txt")
+    _pins.pin_clip_worked_example(_clip_factory(), fixture)
+    for pin in _pins.CLIP_PINS:
+        pin(_clip_factory())
