@@ -178,6 +178,37 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
                     float* const* update_out, float* norms_out,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Workspace size for dmuon_clip_grad_norm, in bytes.  Needs no GPU.
+ */
+int dmuon_clip_grad_norm_workspace_bytes(int count, const int64_t* numel, int num_segments, size_t* bytes_out);
+
+/*
+ * Per-segment global p-norm gradient clipping, in place (training guide,
+ * "梯度裁剪": the Muon clip before momentum and Newton-Schulz, and the fused
+ * bucketed clip that keeps per-segment semantics; the rule of PyTorch's
+ * clip_grad_norm_, which the guide names for the other parameters):
+ *
+ *   total_s = (sum over i with segment[i] == s of sum |g_i|^p)^(1/p)   (max |g_i| for p = +inf)
+ *   coef_s  = min(max_norm[s] / (total_s + 1e-6), 1)
+ *   g_i    <- coef_s * g_i     (a segment with coef_s == 1 is not rewritten)
+ *
+ * grads[i]     : device, numel[i] contiguous elements of `dtype`, updated in
+ *                place (RNE for bf16); distinct buffers.
+ * numel[i]     : >= 0 (0 = an empty tensor, ignored).
+ * segment[i]   : host, in [0, num_segments).
+ * max_norm[s]  : host, finite, >= 0.
+ * norm_type    : p > 0 or +inf.  Totals accumulate in fp32 in a fixed order,
+ *                so results are bitwise reproducible.  A non-finite total
+ *                gives a coefficient of 0 (total +inf) or NaN (total NaN),
+ *                as the reference rule does.
+ * totals_out   : NULL or device float32[num_segments] receiving total_s.
+ * count == 0 enqueues nothing.
+ */
+int dmuon_clip_grad_norm(int count, void* const* grads, const int64_t* numel, int dtype, const int* segment,
+                         int num_segments, const float* max_norm, float norm_type, float* totals_out,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Static text for a status code. */
 const char* dmuon_status_string(int status);
 

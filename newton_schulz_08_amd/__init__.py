@@ -8,6 +8,8 @@ from .api import (  # noqa: F401
     MuonStep,
     alloc_workspace,
     backend_info,
+    clip_grad_norm_,
+    clip_grad_norm_workspace_bytes,
     dtype_code,
     muon_step,
     muon_step_workspace_bytes,

@@ -235,6 +235,48 @@ def muon_step(params, grads, momentum, **kw) -> None:
     MuonStep(params, grads, momentum, **kw)(stream)
 
 
+def clip_grad_norm_workspace_bytes(numels: Sequence[int], num_segments: int = 1) -> int:
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in numels])
+    out = ctypes.c_size_t(0)
+    check(_lib.load().dmuon_clip_grad_norm_workspace_bytes(n, arr, int(num_segments), ctypes.byref(out)),
+          "dmuon_clip_grad_norm_workspace_bytes")
+    return int(out.value)
+
+
+def clip_grad_norm_(grads: Sequence[torch.Tensor], max_norm, segments: Optional[Sequence[int]] = None,
+                    norm_type: float = 2.0, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dmuon_clip_grad_norm: per-segment global p-norm clipping of `grads` in
+    place.  `max_norm` is one float (one segment) or one per segment;
+    `segments[i]` names grads[i]'s segment (default: all in segment 0).
+    Returns the per-segment totals as a float32 device tensor."""
+    n = len(grads)
+    max_norms = [float(max_norm)] if not hasattr(max_norm, "__len__") else [float(v) for v in max_norm]
+    nseg = len(max_norms)
+    seg = [0] * n if segments is None else [int(v) for v in segments]
+    if len(seg) != n:
+        raise ValueError("segments must have one entry per gradient")
+    if n == 0:
+        return torch.zeros(nseg, dtype=torch.float32, device="cuda")
+    dt = grads[0].dtype
+    for i, g in enumerate(grads):
+        if not isinstance(g, torch.Tensor) or not g.is_cuda or not g.is_contiguous() or g.dtype != dt:
+            raise ValueError(f"grads[{i}] must be a contiguous device tensor of dtype {dt}")
+    numel = (ctypes.c_int64 * n)(*[g.numel() for g in grads])
+    segarr = (ctypes.c_int * n)(*seg)
+    mn = (ctypes.c_float * nseg)(*max_norms)
+    totals = torch.empty(nseg, dtype=torch.float32, device=grads[0].device)
+    need = clip_grad_norm_workspace_bytes([g.numel() for g in grads], nseg)
+    if workspace is None:
+        workspace = alloc_workspace(need, grads[0].device)
+    check(_lib.load().dmuon_clip_grad_norm(n, _ptrs(grads), numel, dtype_code(dt), segarr, nseg, mn,
+                                           ctypes.c_float(norm_type), ctypes.c_void_p(totals.data_ptr()),
+                                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                           ctypes.c_void_p(_stream_handle(stream))),
+          "dmuon_clip_grad_norm")
+    return totals
+
+
 def backend_info() -> str:
     return _lib.load().dmuon_backend_info().decode()
 

@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "../../include/dmuon.h"
+#include "clip.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -245,9 +246,9 @@ int check_device() {
 }
 
 // ---------------------------------------------------------------- profiler
-enum KernelClass { kKPrologue = 0, kKNorm, kKSyrk, kKGemm, kKApply, kKSquare, kKNumClasses };
+enum KernelClass { kKPrologue = 0, kKNorm, kKSyrk, kKGemm, kKApply, kKSquare, kKClip, kKNumClasses };
 const char* kClassNames[kKNumClasses] = {"prologue", "norm_finalize", "syrk", "ns_gemm", "apply_x0",
-                                         "syrk_square"};
+                                         "syrk_square", "grad_clip"};
 
 struct ProfRecord {
   int cls;
@@ -531,6 +532,64 @@ int check_distinct(const std::vector<std::pair<const void*, std::string>>& ptrs)
   return DMUON_OK;
 }
 
+// ---------------------------------------------------------------- gradient clipping
+struct ClipPlan {
+  std::vector<int> order;        // tensor indices sorted (stably) by segment
+  std::vector<int> tile_prefix;  // per ordered tensor, size n + 1
+  std::vector<int> seg_tile0;    // per segment, size nseg + 1
+  size_t off_descs = 0, off_prefix = 0, off_seg = 0, off_maxn = 0, off_coef = 0, off_part = 0, total = 0;
+};
+
+int validate_clip(int count, const int64_t* numel, int nseg) {
+  if (count < 0) return fail(DMUON_ERR_INVALID_ARG, "count < 0");
+  if (nseg < 1) return fail(DMUON_ERR_INVALID_ARG, "num_segments must be >= 1");
+  if (count > 0 && !numel) return fail(DMUON_ERR_INVALID_ARG, "numel array is NULL");
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    if (numel[i] < 0) return fail(DMUON_ERR_INVALID_ARG, "numel[" + std::to_string(i) + "] < 0");
+    tiles += (numel[i] + kClipTile - 1) / kClipTile;
+    if (tiles > (int64_t{1} << 30)) return fail(DMUON_ERR_INVALID_ARG, "too many elements in one call");
+  }
+  return DMUON_OK;
+}
+
+// Layout with segments unknown (workspace query) or known (the call).
+ClipPlan make_clip_plan(int count, const int64_t* numel, const int* segment, int nseg) {
+  ClipPlan cp;
+  cp.order.resize(count);
+  for (int i = 0; i < count; ++i) cp.order[i] = i;
+  if (segment) std::stable_sort(cp.order.begin(), cp.order.end(), [&](int a, int b) { return segment[a] < segment[b]; });
+  cp.tile_prefix.assign(count + 1, 0);
+  cp.seg_tile0.assign(nseg + 1, 0);
+  int t = 0, k = 0;
+  for (int s = 0; s < nseg; ++s) {
+    cp.seg_tile0[s] = t;
+    while (k < count && (!segment || segment[cp.order[k]] == s)) {
+      cp.tile_prefix[k] = t;
+      t += static_cast<int>((numel[cp.order[k]] + kClipTile - 1) / kClipTile);
+      ++k;
+    }
+  }
+  for (; k < count; ++k) cp.tile_prefix[k] = t;
+  cp.tile_prefix[count] = t;
+  cp.seg_tile0[nseg] = t;
+  size_t off = 0;
+  cp.off_descs = off;
+  off = align_up(off + sizeof(ClipDesc) * std::max(count, 1));
+  cp.off_prefix = off;
+  off = align_up(off + sizeof(int) * (count + 1));
+  cp.off_seg = off;
+  off = align_up(off + sizeof(int) * (nseg + 1));
+  cp.off_maxn = off;
+  off = align_up(off + sizeof(float) * nseg);
+  cp.off_coef = off;
+  off = align_up(off + sizeof(float) * nseg);
+  cp.off_part = off;
+  off = align_up(off + sizeof(float) * std::max(t, 1));
+  cp.total = off;
+  return cp;
+}
+
 int ws_check(const Plan& pl, void* workspace, size_t bytes) {
   if (!workspace) return fail(DMUON_ERR_WORKSPACE, "workspace is NULL");
   if (bytes < pl.total)
@@ -655,6 +714,88 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
   call.nesterov = nesterov ? 1 : 0;
   call.ns = ns;
   return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+int dmuon_clip_grad_norm_workspace_bytes(int count, const int64_t* numel, int num_segments, size_t* bytes_out) {
+  g_last_error.clear();
+  if (!bytes_out) return fail(DMUON_ERR_INVALID_ARG, "bytes_out is NULL");
+  int st = validate_clip(count, numel, num_segments);
+  if (st != DMUON_OK) return st;
+  *bytes_out = count == 0 ? 0 : make_clip_plan(count, numel, nullptr, num_segments).total;
+  return DMUON_OK;
+}
+
+int dmuon_clip_grad_norm(int count, void* const* grads, const int64_t* numel, int dtype, const int* segment,
+                         int num_segments, const float* max_norm, float norm_type, float* totals_out,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_last_error.clear();
+  int st = validate_clip(count, numel, num_segments);
+  if (st != DMUON_OK) return st;
+  if (dtype != kF32 && dtype != kBF16)
+    return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "dtype must be DMUON_F32 or DMUON_BF16");
+  if (!(norm_type > 0.0f)) return fail(DMUON_ERR_INVALID_ARG, "norm_type must be > 0 (or +inf)");
+  if (!max_norm) return fail(DMUON_ERR_INVALID_ARG, "max_norm array is NULL");
+  for (int s = 0; s < num_segments; ++s)
+    if (!std::isfinite(max_norm[s]) || max_norm[s] < 0.0f)
+      return fail(DMUON_ERR_INVALID_ARG, "max_norm entries must be finite and >= 0");
+  if (count == 0) return DMUON_OK;
+  if (!segment) return fail(DMUON_ERR_INVALID_ARG, "segment array is NULL");
+  if (!grads) return fail(DMUON_ERR_INVALID_ARG, "grads array is NULL");
+  std::vector<std::pair<const void*, std::string>> ptrs;
+  for (int i = 0; i < count; ++i) {
+    if (segment[i] < 0 || segment[i] >= num_segments)
+      return fail(DMUON_ERR_INVALID_ARG, "segment[" + std::to_string(i) + "] outside [0, num_segments)");
+    if (numel[i] > 0 && !grads[i]) return fail(DMUON_ERR_INVALID_ARG, "grads[" + std::to_string(i) + "] is NULL");
+    if (numel[i] > 0) ptrs.push_back({grads[i], "grads[" + std::to_string(i) + "]"});
+  }
+  if ((st = check_distinct(ptrs)) != DMUON_OK) return st;
+  const ClipPlan cp = make_clip_plan(count, numel, segment, num_segments);
+  if (!workspace) return fail(DMUON_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < cp.total)
+    return fail(DMUON_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                         std::to_string(cp.total));
+  if (!aligned(workspace, kAlign)) return fail(DMUON_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((st = check_device()) != DMUON_OK) return st;
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  std::vector<ClipDesc> descs(count);
+  double bytes = 0.0;
+  for (int k = 0; k < count; ++k) {
+    const int i = cp.order[k];
+    ClipDesc& d = descs[k];
+    std::memset(&d, 0, sizeof(d));
+    d.g = grads[i];
+    d.numel = numel[i];
+    d.segment = segment[i];
+    d.vec_ok = aligned(grads[i], 16) ? 1 : 0;
+    bytes += static_cast<double>(numel[i]) * elem_bytes(dtype);
+  }
+  ClipDesc* d_descs = reinterpret_cast<ClipDesc*>(ws + cp.off_descs);
+  int* d_prefix = reinterpret_cast<int*>(ws + cp.off_prefix);
+  int* d_seg = reinterpret_cast<int*>(ws + cp.off_seg);
+  float* d_maxn = reinterpret_cast<float*>(ws + cp.off_maxn);
+  float* d_coef = reinterpret_cast<float*>(ws + cp.off_coef);
+  float* d_part = reinterpret_cast<float*>(ws + cp.off_part);
+  if (hipMemcpyAsync(d_descs, descs.data(), sizeof(ClipDesc) * count, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(d_prefix, cp.tile_prefix.data(), sizeof(int) * (count + 1), hipMemcpyHostToDevice, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(d_seg, cp.seg_tile0.data(), sizeof(int) * (num_segments + 1), hipMemcpyHostToDevice, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(d_maxn, max_norm, sizeof(float) * num_segments, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return fail(DMUON_ERR_HIP, std::string("clip descriptor upload failed: ") + hipGetErrorString(hipGetLastError()));
+  const int kind = std::isinf(norm_type) ? kClipPInf
+                   : norm_type == 2.0f    ? kClipP2
+                   : norm_type == 1.0f    ? kClipP1
+                                          : kClipPGeneral;
+  const int tiles = cp.tile_prefix[count];
+  const int grid = std::max(1, std::min(tiles, 256 * 8));
+  hipError_t e = timed(kKClip, 0.0, bytes, stream, [&] {
+    return launch_clip(dtype, d_descs, d_prefix, count, tiles, d_seg, num_segments, d_maxn, kind, norm_type, d_part,
+                       d_coef, totals_out, grid, stream);
+  });
+  if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("clip launch: ") + hipGetErrorString(e));
+  return DMUON_OK;
 }
 
 const char* dmuon_status_string(int status) {

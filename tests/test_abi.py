@@ -198,3 +198,30 @@ def test_profile_read_empty(lib):
     n = ctypes.c_int(-1)
     assert lib.dmuon_profile_read(stats, 4, ctypes.byref(n)) == 0
     assert n.value == 0
+
+
+def test_clip_workspace_and_validation(lib):
+    E = _lib
+    n = (ctypes.c_int64 * 3)(4096, 10, 0)
+    out = ctypes.c_size_t(0)
+    assert lib.dmuon_clip_grad_norm_workspace_bytes(3, n, 2, ctypes.byref(out)) == 0
+    # descriptors, prefix, segment starts, max_norm, coefficients, 2 tile partials: 256-aligned regions
+    assert out.value == 6 * 256
+    assert lib.dmuon_clip_grad_norm_workspace_bytes(3, n, 0, ctypes.byref(out)) == E.DMUON_ERR_INVALID_ARG
+    bad = (ctypes.c_int64 * 1)(-1)
+    assert lib.dmuon_clip_grad_norm_workspace_bytes(1, bad, 1, ctypes.byref(out)) == E.DMUON_ERR_INVALID_ARG
+    P = (ctypes.c_void_p * 2)
+    nn = (ctypes.c_int64 * 2)(8, 8)
+    seg = (ctypes.c_int * 2)(0, 1)
+    mn = (ctypes.c_float * 2)(1.0, 1.0)
+    call = lambda ptrs=P(0x1000, 0x2000), segs=seg, m=mn, p=2.0, dt=0, nseg=2, ws=None: lib.dmuon_clip_grad_norm(  # noqa: E731
+        2, ptrs, nn, dt, segs, nseg, m, ctypes.c_float(p), None, ws, 1 << 20, None)
+    assert call(p=0.0) == E.DMUON_ERR_INVALID_ARG
+    assert call(p=float("nan")) == E.DMUON_ERR_INVALID_ARG
+    assert call(dt=5) == E.DMUON_ERR_UNSUPPORTED_DTYPE
+    assert call(segs=(ctypes.c_int * 2)(0, 2)) == E.DMUON_ERR_INVALID_ARG
+    assert call(m=(ctypes.c_float * 2)(1.0, -1.0)) == E.DMUON_ERR_INVALID_ARG
+    assert call(ptrs=P(0x1000, 0x1000)) == E.DMUON_ERR_INVALID_ARG
+    assert "alias" in _lib.last_error()
+    assert call() == E.DMUON_ERR_WORKSPACE
+    assert call(ws=0x100010) == E.DMUON_ERR_WORKSPACE
