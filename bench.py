@@ -118,6 +118,32 @@ def metadata(torch):
     return meta
 
 
+def clip_bench(torch, nsa, grads, reps=5):
+    """Per-segment gradient clipping over the whole gradient set (one segment
+    per projection kind): an unclipped pass (read only) and a clipping pass
+    (read, then read and write), timed by the library's kernel events."""
+    kinds = sorted({g.shape for g in grads})
+    segs = [kinds.index(g.shape) for g in grads]
+    numel = sum(g.numel() for g in grads)
+    eb = grads[0].element_size()
+    ws = nsa.alloc_workspace(nsa.clip_grad_norm_workspace_bytes([g.numel() for g in grads], len(kinds)))
+    out = {"tensors": len(grads), "segments": len(kinds), "elements": numel}
+    for tag, max_norm, bytes_per in (("no_clip", 1e30, eb), ("clip", 0.0, 3 * eb)):
+        nsa.clip_grad_norm_(grads, [max_norm] * len(kinds), segs, workspace=ws)
+        torch.cuda.synchronize()
+        nsa.profile_read()
+        nsa.profile_enable(True)
+        for _ in range(reps):
+            nsa.clip_grad_norm_(grads, [max_norm] * len(kinds), segs, workspace=ws)
+        torch.cuda.synchronize()
+        nsa.profile_enable(False)
+        st = nsa.profile_read().get("grad_clip")
+        ms = st["total_ms"] / st["launches"]
+        gbs = numel * bytes_per / (ms * 1e-3) / 1e9
+        out[tag] = {"ms": ms, "algorithmic_bytes": numel * bytes_per, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+    return out
+
+
 def reference_gemm(torch, n=8192, reps=30):
     """Context only: torch.matmul (hipBLASLt) on an n^3 bf16 GEMM of random data on the same GPU, sustained
     over ~1 s, to show the practical power-limited MFMA rate next to the published peak."""
@@ -153,6 +179,7 @@ def main():
                     help="Newton-Schulz polynomial (default: the cubic 1.5, -0.5)")
     ap.add_argument("--weight-decay", type=float, default=0.0)
     ap.add_argument("--moonlight", action="store_true", help="scale lr by 0.2*sqrt(max(m, n)) per matrix")
+    ap.add_argument("--no-clip-bench", action="store_true", help="skip timing per-segment gradient clipping")
     ap.add_argument("--full-gram", action="store_true",
                     help="ablation: compute every Gram tile instead of the lower triangle plus its mirror")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -282,6 +309,9 @@ def main():
         "backend": nsa.backend_info(),
         "meta": metadata(torch),
     }
+    if not args.no_clip_bench:
+        # after the timed steps: the clipping pass rescales the gradients in place
+        out["grad_clip"] = clip_bench(torch, nsa, grads)
     if not args.no_reference_gemm and cfg.dtype == "bf16":
         out["reference_gemm"] = reference_gemm(torch)
     if not args.no_cpu_baseline:

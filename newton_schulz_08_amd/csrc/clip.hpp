@@ -8,7 +8,7 @@
 
 namespace dmuon {
 
-constexpr int kClipTile = 4096;     // elements per partial-sum tile
+constexpr int kClipTile = 16384;    // elements per partial-sum tile: 8 (bf16) or 16 (fp32) 16-byte loads per thread
 constexpr int kClipThreads = 256;
 constexpr float kClipEps = 1e-6f;   // the +1e-6 of the clipping rule
 

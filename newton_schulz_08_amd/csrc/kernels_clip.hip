@@ -11,7 +11,7 @@
 //   g      <- coef_s * g
 //
 // Three launches: clip_partials_kernel reads every gradient once and writes
-// one partial per 4096-element tile; clip_finalize_kernel reduces each
+// one partial per 16384-element tile; clip_finalize_kernel reduces each
 // segment's tiles in a fixed order (tensors are ordered by segment, so a
 // segment's tiles are contiguous); clip_scale_kernel rewrites only tiles whose
 // coefficient is below 1, so an unclipped step costs one read pass.
@@ -38,14 +38,13 @@ __device__ __forceinline__ int find_tensor(const int* __restrict__ prefix, int n
 }
 
 // |x|^p accumulated into acc (sum), or max for p = inf.
-__device__ __forceinline__ float accum(float acc, float x, int kind, float p) {
+template <int KIND>
+__device__ __forceinline__ float accum(float acc, float x, float p) {
   const float a = fabsf(x);
-  switch (kind) {
-    case kClipP2: return fmaf(a, a, acc);
-    case kClipP1: return acc + a;
-    case kClipPInf: return fmaxf(acc, a);
-    default: return acc + powf(a, p);
-  }
+  if constexpr (KIND == kClipP2) return fmaf(a, a, acc);
+  else if constexpr (KIND == kClipP1) return acc + a;
+  else if constexpr (KIND == kClipPInf) return fmaxf(acc, a);
+  else return acc + powf(a, p);
 }
 
 __device__ __forceinline__ float combine(float a, float b, int kind) { return kind == kClipPInf ? fmaxf(a, b) : a + b; }
@@ -67,6 +66,15 @@ __device__ __forceinline__ float block_reduce(float v, int kind, float* red) {
   for (int w = 1; w < kClipThreads / 64; ++w) r = combine(r, red[w], kind);
   __syncthreads();
   return r;
+}
+
+template <typename T> struct RawVec;
+template <> struct RawVec<float> { using V = f32v4; };
+template <> struct RawVec<__bf16> { using V = bf16x8_t; };
+
+template <typename T>
+__device__ __forceinline__ typename RawVec<T>::V load_raw(const T* p) {
+  return *reinterpret_cast<gptr<const typename RawVec<T>::V>>(gmem(p));
 }
 
 template <typename T>
@@ -96,13 +104,14 @@ __device__ __forceinline__ void store_vec<__bf16>(__bf16* p, const float* v) {
   *reinterpret_cast<gptr<bf16x8_t>>(gmem(p)) = x;
 }
 
-template <int DT>
+template <int DT, int KIND>
 __global__ __launch_bounds__(kClipThreads) void clip_partials_kernel(const ClipDesc* __restrict__ descs,
                                                                      const int* __restrict__ prefix, int n,
                                                                      int total_tiles, float* __restrict__ partials,
-                                                                     int kind, float p) {
+                                                                     float p) {
   using T = typename ClipElem<DT>::T;
   constexpr int V = ClipElem<DT>::kVec;
+  constexpr int kIters = kClipTile / (kClipThreads * V);
   __shared__ float red[kClipThreads / 64];
   for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
     const int i = find_tensor(prefix, n, t);
@@ -110,21 +119,25 @@ __global__ __launch_bounds__(kClipThreads) void clip_partials_kernel(const ClipD
     const int64_t base = static_cast<int64_t>(t - prefix[i]) * kClipTile;
     const T* g = static_cast<const T*>(d.g);
     float acc = 0.0f;
-    // wave instruction k covers 64 consecutive vectors: one contiguous KB
+    if (d.vec_ok && base + kClipTile <= d.numel) {
+      // whole tile: every load in flight before any arithmetic; wave
+      // instruction k covers 64 consecutive vectors (one contiguous KB)
+      typename RawVec<T>::V raw[kIters];
 #pragma unroll
-    for (int k = 0; k < kClipTile / (kClipThreads * V); ++k) {
-      const int64_t e0 = base + (static_cast<int64_t>(k) * kClipThreads + threadIdx.x) * V;
-      if (d.vec_ok && e0 + V <= d.numel) {
-        float v[V];
-        load_vec<T>(g + e0, v);
+      for (int k = 0; k < kIters; ++k) raw[k] = load_raw<T>(g + base + (k * kClipThreads + threadIdx.x) * V);
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc = accum(acc, v[e], kind, p);
-      } else {
+      for (int k = 0; k < kIters; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc = accum<KIND>(acc, static_cast<float>(raw[k][e]), p);
+    } else {
+      // a tensor's last (partial) tile, or an unaligned tensor
+      for (int k = 0; k < kIters; ++k) {
+        const int64_t e0 = base + (static_cast<int64_t>(k) * kClipThreads + threadIdx.x) * V;
         for (int e = 0; e < V; ++e)
-          if (e0 + e < d.numel) acc = accum(acc, static_cast<float>(gmem(g)[e0 + e]), kind, p);
+          if (e0 + e < d.numel) acc = accum<KIND>(acc, static_cast<float>(gmem(g)[e0 + e]), p);
       }
     }
-    const float r = block_reduce(acc, kind, red);
+    const float r = block_reduce(acc, KIND, red);
     if (threadIdx.x == 0) partials[t] = r;
   }
 }
@@ -158,6 +171,7 @@ __global__ __launch_bounds__(kClipThreads) void clip_scale_kernel(const ClipDesc
                                                                   int total_tiles, const float* __restrict__ coefs) {
   using T = typename ClipElem<DT>::T;
   constexpr int V = ClipElem<DT>::kVec;
+  constexpr int kIters = kClipTile / (kClipThreads * V);
   for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
     const int i = find_tensor(prefix, n, t);
     const ClipDesc& d = descs[i];
@@ -165,16 +179,20 @@ __global__ __launch_bounds__(kClipThreads) void clip_scale_kernel(const ClipDesc
     if (c == 1.0f) continue;  // uniform per tile: an unclipped segment is not rewritten
     const int64_t base = static_cast<int64_t>(t - prefix[i]) * kClipTile;
     T* g = static_cast<T*>(d.g);
+    if (d.vec_ok && base + kClipTile <= d.numel) {
+      typename RawVec<T>::V raw[kIters];
 #pragma unroll
-    for (int k = 0; k < kClipTile / (kClipThreads * V); ++k) {
-      const int64_t e0 = base + (static_cast<int64_t>(k) * kClipThreads + threadIdx.x) * V;
-      if (d.vec_ok && e0 + V <= d.numel) {
+      for (int k = 0; k < kIters; ++k) raw[k] = load_raw<T>(g + base + (k * kClipThreads + threadIdx.x) * V);
+#pragma unroll
+      for (int k = 0; k < kIters; ++k) {
         float v[V];
-        load_vec<T>(g + e0, v);
 #pragma unroll
-        for (int e = 0; e < V; ++e) v[e] *= c;
-        store_vec<T>(g + e0, v);
-      } else {
+        for (int e = 0; e < V; ++e) v[e] = static_cast<float>(raw[k][e]) * c;
+        store_vec<T>(g + base + (k * kClipThreads + threadIdx.x) * V, v);
+      }
+    } else {
+      for (int k = 0; k < kIters; ++k) {
+        const int64_t e0 = base + (static_cast<int64_t>(k) * kClipThreads + threadIdx.x) * V;
         for (int e = 0; e < V; ++e)
           if (e0 + e < d.numel) gmem(g)[e0 + e] = static_cast<T>(static_cast<float>(gmem(g)[e0 + e]) * c);
       }
@@ -188,12 +206,25 @@ hipError_t launch_clip(int dt, const ClipDesc* descs, const int* tile_prefix, in
                        const int* seg_tile0, int nseg, const float* max_norm, int kind, float p, float* partials,
                        float* coefs, float* totals_out, int grid, hipStream_t stream) {
   if (total_tiles > 0) {
-    if (dt == kBF16)
-      hipLaunchKernelGGL(clip_partials_kernel<kBF16>, dim3(grid), dim3(kClipThreads), 0, stream, descs, tile_prefix, n,
-                         total_tiles, partials, kind, p);
-    else
-      hipLaunchKernelGGL(clip_partials_kernel<kF32>, dim3(grid), dim3(kClipThreads), 0, stream, descs, tile_prefix, n,
-                         total_tiles, partials, kind, p);
+    auto partials_launch = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(grid), dim3(kClipThreads), 0, stream, descs, tile_prefix, n, total_tiles,
+                         partials, p);
+    };
+    if (dt == kBF16) {
+      switch (kind) {
+        case kClipP2: partials_launch(clip_partials_kernel<kBF16, kClipP2>); break;
+        case kClipP1: partials_launch(clip_partials_kernel<kBF16, kClipP1>); break;
+        case kClipPInf: partials_launch(clip_partials_kernel<kBF16, kClipPInf>); break;
+        default: partials_launch(clip_partials_kernel<kBF16, kClipPGeneral>); break;
+      }
+    } else {
+      switch (kind) {
+        case kClipP2: partials_launch(clip_partials_kernel<kF32, kClipP2>); break;
+        case kClipP1: partials_launch(clip_partials_kernel<kF32, kClipP1>); break;
+        case kClipPInf: partials_launch(clip_partials_kernel<kF32, kClipPInf>); break;
+        default: partials_launch(clip_partials_kernel<kF32, kClipPGeneral>); break;
+      }
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
