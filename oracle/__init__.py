@@ -23,6 +23,7 @@ from .muon import (  # noqa: F401
     CLIP_EPS,
     CUBIC,
     EPS,
+    adamw_step,
     MIN_NS_NUMEL,
     apply_update,
     clip_grad_norm_buckets,

@@ -28,6 +28,9 @@ reason, in the design notes of the repository):
 * Gradient clipping (training guide, "梯度裁剪") follows the global p-norm rule
   of torch.nn.utils.clip_grad_norm_, which the guide names for the other
   parameters, applied per segment.
+* The AdamW route for non-matrix parameters ("standard" in the training guide)
+  follows PyTorch's AdamW: decoupled decay, bias-corrected moments, eps added
+  after the bias-corrected square root, step counted from 1.
 """
 from __future__ import annotations
 
@@ -231,6 +234,31 @@ def clip_grad_norm_buckets(grads: Sequence[np.ndarray], segments: Sequence[int],
         coef = min(float(max_norms[s]) / (totals[s] + CLIP_EPS), 1.0)
         out.append(g * coef)
     return out, totals
+
+
+def adamw_step(p, g, m, v, step: int, lr: float, beta1: float, beta2: float, eps: float,
+               weight_decay: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One AdamW step for a non-matrix parameter (training guide: group 1,
+    "AdamW — 标准", with ``adamw_lr``, ``adamw_betas``, ``adamw_eps`` and
+    ``adamw_weight_decay``).  "Standard" is read as PyTorch's AdamW:
+
+        p <- p (1 - lr wd)
+        m <- beta1 m + (1 - beta1) g
+        v <- beta2 v + (1 - beta2) g^2
+        p <- p - (lr / (1 - beta1^t)) m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+
+    with the step counter t = ``step`` >= 1.  Returns (p, m, v).
+    """
+    if step < 1:
+        raise ValueError("step counts from 1")
+    p = np.asarray(p, dtype=np.float64) * (1.0 - lr * weight_decay)
+    g = np.asarray(g, dtype=np.float64)
+    m = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    bc1 = 1.0 - beta1 ** step
+    bc2 = 1.0 - beta2 ** step
+    denom = np.sqrt(v) / np.sqrt(bc2) + eps
+    return p - (lr / bc1) * m / denom, m, v
 
 
 def orthogonality_error(x) -> float:

@@ -519,3 +519,53 @@ def pin_clip_loops(clip, seed=67):
 
 
 CLIP_PINS = [pin_clip_closed_forms, pin_clip_loops]
+
+
+# ----------------------------------------------------------------------------- AdamW
+def pin_adamw_worked_example(adamw, fixture):
+    """tests/golden/adamw_worked_example.txt, bit for bit."""
+    h = {k: v[0] for k, v in fixture.items()}
+    args = (h["lr"], h["beta1"], h["beta2"], h["eps"], h["wd"])
+    p1, m1, v1 = adamw(np.array([h["p0"]]), np.array([h["g1"]]), np.zeros(1), np.zeros(1), 1, *args)
+    assert (p1[0], m1[0], v1[0]) == (h["p1"], h["m1"], h["v1"])
+    p2, m2, v2 = adamw(p1, np.array([h["g2"]]), m1, v1, 2, *args)
+    assert (p2[0], m2[0], v2[0]) == (h["p2"], h["m2"], h["v2"])
+
+
+def pin_adamw_closed_forms(adamw, seed=71):
+    rng = np.random.default_rng(seed)
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.999, 1e-8, 0.01
+    p0, g = rng.standard_normal((2, 50))
+    # a constant gradient from a zero state: the bias-corrected moments are g
+    # and g^2 at every step, so each step decays p and subtracts lr g / (|g| + eps)
+    p, m, v = p0.copy(), np.zeros(50), np.zeros(50)
+    want = p0.copy()
+    for t in range(1, 8):
+        p, m, v = adamw(p, g, m, v, t, lr, b1, b2, eps, wd)
+        want = want * (1 - lr * wd) - lr * g / (np.abs(g) + eps)
+        assert np.allclose(m, (1 - b1 ** t) * g, rtol=1e-14, atol=0)
+        assert np.allclose(v, (1 - b2 ** t) * g * g, rtol=1e-12, atol=0)
+        assert np.allclose(p, want, rtol=1e-12, atol=1e-15), t
+    # a zero gradient from a zero state only decays
+    p, m, v = adamw(p0, np.zeros(50), np.zeros(50), np.zeros(50), 1, lr, b1, b2, eps, wd)
+    assert np.array_equal(p, p0 * (1 - lr * wd)) and not m.any() and not v.any()
+
+
+def pin_adamw_loops(adamw, seed=73):
+    rng = np.random.default_rng(seed)
+    lr, b1, b2, eps, wd = 3e-3, 0.8, 0.95, 1e-6, 0.1
+    p, m, v = rng.standard_normal(5), np.zeros(5), np.zeros(5)
+    ref = [float(x) for x in p]
+    rm, rv = [0.0] * 5, [0.0] * 5
+    for t in range(1, 4):
+        g = rng.standard_normal(5)
+        p, m, v = adamw(p, g, m, v, t, lr, b1, b2, eps, wd)
+        for j in range(5):
+            ref[j] *= 1 - lr * wd
+            rm[j] = b1 * rm[j] + (1 - b1) * float(g[j])
+            rv[j] = b2 * rv[j] + (1 - b2) * float(g[j]) ** 2
+            ref[j] -= lr / (1 - b1 ** t) * rm[j] / (math.sqrt(rv[j]) / math.sqrt(1 - b2 ** t) + eps)
+        assert np.allclose(p, ref, rtol=1e-13, atol=0)
+
+
+ADAMW_PINS = [pin_adamw_closed_forms, pin_adamw_loops]

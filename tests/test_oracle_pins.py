@@ -63,6 +63,15 @@ def test_grad_clip_rejects_bad_segments():
         oracle.clip_grad_norm_buckets([np.ones(3)], [0], [1.0], norm_type=0.0)
 
 
+def test_adamw_worked_example(golden):
+    _pins.pin_adamw_worked_example(oracle.adamw_step, golden("adamw_worked_example.txt"))
+
+
+@pytest.mark.parametrize("pin", _pins.ADAMW_PINS, ids=lambda f: f.__name__)
+def test_adamw_pin(pin):
+    pin(oracle.adamw_step)
+
+
 def test_momentum_geometric_series():
     _pins.pin_geometric_series(oracle.momentum_update, oracle.ns_input)
 

@@ -215,3 +215,43 @@ def test_unmutated_clip_copy_passes(golden):
     _pins.pin_clip_worked_example(_clip_factory(), fixture)
     for pin in _pins.CLIP_PINS:
         pin(_clip_factory())
+
+
+# ----------------------------------------------------------------------------- AdamW
+def _adamw_factory(no_bias=False, coupled=False, eps_inside=False, decay_after=False):
+    def adamw(p, g, m, v, step, lr, b1, b2, eps, wd):
+        p = np.asarray(p, dtype=np.float64)
+        g = np.asarray(g, dtype=np.float64)
+        if coupled:
+            g = g + wd * p
+        elif not decay_after:
+            p = p * (1 - lr * wd)
+        m = b1 * np.asarray(m) + (1 - b1) * g
+        v = b2 * np.asarray(v) + (1 - b2) * g * g
+        bc1, bc2 = (1.0, 1.0) if no_bias else (1 - b1 ** step, 1 - b2 ** step)
+        denom = np.sqrt(v / bc2 + eps) if eps_inside else np.sqrt(v) / np.sqrt(bc2) + eps
+        p = p - lr / bc1 * m / denom
+        if decay_after:
+            p = p * (1 - lr * wd)
+        return p, m, v
+    return adamw
+
+
+ADAMW_MUTANTS = {"no_bias_correction": _adamw_factory(no_bias=True), "coupled_decay": _adamw_factory(coupled=True),
+                 "eps_inside_sqrt": _adamw_factory(eps_inside=True), "decay_after": _adamw_factory(decay_after=True)}
+
+
+@pytest.mark.parametrize("name", sorted(ADAMW_MUTANTS))
+def test_adamw_mutant_is_caught(name, golden):
+    fixture = golden("adamw_worked_example.txt")
+    mutant = ADAMW_MUTANTS[name]
+    caught = _caught(lambda: _pins.pin_adamw_worked_example(mutant, fixture))
+    for pin in _pins.ADAMW_PINS:
+        caught = caught or _caught(lambda: pin(mutant))
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_adamw_copy_passes(golden):
+    _pins.pin_adamw_worked_example(_adamw_factory(), golden("adamw_worked_example.txt"))
+    for pin in _pins.ADAMW_PINS:
+        pin(_adamw_factory())
