@@ -144,6 +144,44 @@ def clip_bench(torch, nsa, grads, reps=5):
     return out
 
 
+# Llama-3-8B's non-matrix parameters, which go to AdamW: token embedding and
+# output head (128256 x 4096 each) and 65 RMSNorm weights of 4096.
+ADAMW_SET = [128256 * 4096, 128256 * 4096] + [4096] * 65
+
+
+def adamw_bench(torch, nsa, dtype, reps=10):
+    """The fused AdamW step over the non-matrix parameter set, seeded synthetic
+    values, timed by the library's kernel events.  Algorithmic bytes per
+    element: parameters and gradients in `dtype`, fp32 moments; read p, g, m, v
+    and write p, m, v."""
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    eb = torch.empty((), dtype=dtype).element_size()
+    P = [torch.randn(n, device="cuda", generator=gen).mul_(0.02).to(dtype) for n in ADAMW_SET]
+    G = [torch.randn(n, device="cuda", generator=gen).mul_(1e-3).to(dtype) for n in ADAMW_SET]
+    M = [torch.zeros(n, device="cuda") for n in ADAMW_SET]
+    V = [torch.zeros(n, device="cuda") for n in ADAMW_SET]
+    ws = nsa.alloc_workspace(nsa.adamw_step_workspace_bytes(ADAMW_SET))
+    numel = sum(ADAMW_SET)
+    bytes_per = 3 * eb + 16
+    nsa.adamw_step_(P, G, M, V, 1, workspace=ws)
+    torch.cuda.synchronize()
+    nsa.profile_read()
+    nsa.profile_enable(True)
+    for t in range(reps):
+        nsa.adamw_step_(P, G, M, V, 2 + t, workspace=ws)
+    torch.cuda.synchronize()
+    nsa.profile_enable(False)
+    st = nsa.profile_read().get("adamw")
+    ms = st["total_ms"] / st["launches"]
+    gbs = numel * bytes_per / (ms * 1e-3) / 1e9
+    out = {"tensors": len(ADAMW_SET), "elements": numel, "param_dtype": str(dtype).replace("torch.", ""),
+           "hyper": "lr 1e-3, betas (0.9, 0.999), eps 1e-8, weight_decay 0.01", "ms": ms,
+           "algorithmic_bytes": numel * bytes_per, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+    del P, G, M, V, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def reference_gemm(torch, n=8192, reps=30):
     """Context only: torch.matmul (hipBLASLt) on an n^3 bf16 GEMM of random data on the same GPU, sustained
     over ~1 s, to show the practical power-limited MFMA rate next to the published peak."""
@@ -180,6 +218,8 @@ def main():
     ap.add_argument("--weight-decay", type=float, default=0.0)
     ap.add_argument("--moonlight", action="store_true", help="scale lr by 0.2*sqrt(max(m, n)) per matrix")
     ap.add_argument("--no-clip-bench", action="store_true", help="skip timing per-segment gradient clipping")
+    ap.add_argument("--no-adamw-bench", action="store_true",
+                    help="skip timing the AdamW step over the non-matrix parameter set")
     ap.add_argument("--full-gram", action="store_true",
                     help="ablation: compute every Gram tile instead of the lower triangle plus its mirror")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -312,6 +352,8 @@ def main():
     if not args.no_clip_bench:
         # after the timed steps: the clipping pass rescales the gradients in place
         out["grad_clip"] = clip_bench(torch, nsa, grads)
+    if not args.no_adamw_bench:
+        out["adamw"] = adamw_bench(torch, nsa, torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)
     if not args.no_reference_gemm and cfg.dtype == "bf16":
         out["reference_gemm"] = reference_gemm(torch)
     if not args.no_cpu_baseline:

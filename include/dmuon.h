@@ -209,6 +209,44 @@ int dmuon_clip_grad_norm(int count, void* const* grads, const int64_t* numel, in
                          int num_segments, const float* max_norm, float norm_type, float* totals_out,
                          void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Workspace size for dmuon_adamw_step, in bytes.  Needs no GPU.
+ */
+int dmuon_adamw_step_workspace_bytes(int count, const int64_t* numel, size_t* bytes_out);
+
+/*
+ * One AdamW step over `count` non-matrix parameters, in place (training
+ * guide, "第 4 步：创建优化器": the parameters Muon does not take form a
+ * standard AdamW group with adamw_lr, adamw_betas, adamw_eps and
+ * adamw_weight_decay; blog post, section "为什么需要矩阵感知优化器": the
+ * update subtracts alpha m_hat / (sqrt(v_hat) + eps) with bias-corrected
+ * moments).  Read as PyTorch's AdamW, per element in fp32:
+ *
+ *   p <- p (1 - lr weight_decay)
+ *   m <- beta1 m + (1 - beta1) g
+ *   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - (lr / (1 - beta1^step)) m / (sqrt(v) / sqrt(1 - beta2^step) + eps)
+ *
+ * params[i]     : device, numel[i] contiguous elements of `dtype`; updated in
+ *                 place (RNE for bf16).
+ * grads[i]      : device, numel[i] elements of `dtype`; read only.
+ * exp_avg[i], exp_avg_sq[i] : device, numel[i] float32 moments, updated in
+ *                 place.  Start both from zeros.
+ * numel[i]      : >= 0 (0 = an empty tensor, ignored; its pointers may be NULL).
+ * step          : the step counter t >= 1 of this update (1 on the first call).
+ * lr, weight_decay : finite.  beta1, beta2 in [0, 1).  eps finite, >= 0.
+ *                 The pages' defaults: lr 1e-3, betas (0.9, 0.999), eps 1e-8,
+ *                 weight_decay 0.01.
+ * All buffers must be distinct and aligned to their element size; 16-byte
+ * alignment (8-byte for bf16 parameters and gradients) takes the vector path.
+ * The bias corrections and 1 - lr weight_decay are formed in double on the
+ * host and rounded to float once.  count == 0 enqueues nothing.
+ */
+int dmuon_adamw_step(int count, void* const* params, const void* const* grads, float* const* exp_avg,
+                     float* const* exp_avg_sq, const int64_t* numel, int dtype, int step, float lr, float beta1,
+                     float beta2, float eps, float weight_decay, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
+
 /* Static text for a status code. */
 const char* dmuon_status_string(int status);
 

@@ -5,7 +5,10 @@ this package is its thin Python binding.  Build the library with
 ``python -m newton_schulz_08_amd.build``.
 """
 from .api import (  # noqa: F401
+    AdamWStep,
     MuonStep,
+    adamw_step_,
+    adamw_step_workspace_bytes,
     alloc_workspace,
     backend_info,
     clip_grad_norm_,

@@ -74,6 +74,10 @@ SIGNATURES = {
     "dmuon_clip_grad_norm_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, ctypes.c_int, _SZP]),
     "dmuon_clip_grad_norm": (ctypes.c_int, [ctypes.c_int, _PP, _I64P, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                             ctypes.c_int, _FP, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
+    "dmuon_adamw_step_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, _SZP]),
+    "dmuon_adamw_step": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _PP, _I64P, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dmuon_last_error": (ctypes.c_char_p, []),
     "dmuon_backend_info": (ctypes.c_char_p, []),

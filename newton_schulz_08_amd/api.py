@@ -277,6 +277,68 @@ def clip_grad_norm_(grads: Sequence[torch.Tensor], max_norm, segments: Optional[
     return totals
 
 
+def adamw_step_workspace_bytes(numels: Sequence[int]) -> int:
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in numels])
+    out = ctypes.c_size_t(0)
+    check(_lib.load().dmuon_adamw_step_workspace_bytes(n, arr, ctypes.byref(out)), "dmuon_adamw_step_workspace_bytes")
+    return int(out.value)
+
+
+def adamw_step_(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], exp_avg: Sequence[torch.Tensor],
+                exp_avg_sq: Sequence[torch.Tensor], step: int, lr: float = 1e-3, betas=(0.9, 0.999),
+                eps: float = 1e-8, weight_decay: float = 0.01, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """dmuon_adamw_step: one AdamW step over every tensor, in place.  The
+    moments are float32 tensors shaped like the parameters; `step` counts
+    from 1.  Defaults are the training guide's adamw_* settings."""
+    n = len(params)
+    if not (len(grads) == len(exp_avg) == len(exp_avg_sq) == n):
+        raise ValueError("params, grads, exp_avg and exp_avg_sq must have the same length")
+    if n == 0:
+        return
+    dt = params[0].dtype
+    for i in range(n):
+        for name, t, want in (("params", params[i], dt), ("grads", grads[i], dt), ("exp_avg", exp_avg[i], torch.float32),
+                              ("exp_avg_sq", exp_avg_sq[i], torch.float32)):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dtype != want:
+                raise ValueError(f"{name}[{i}] must be a contiguous device tensor of dtype {want}")
+            if t.numel() != params[i].numel():
+                raise ValueError(f"{name}[{i}] has {t.numel()} elements, params[{i}] has {params[i].numel()}")
+    numels = [p.numel() for p in params]
+    numel = (ctypes.c_int64 * n)(*numels)
+    if workspace is None:
+        workspace = alloc_workspace(adamw_step_workspace_bytes(numels), params[0].device)
+    b1, b2 = betas
+    check(_lib.load().dmuon_adamw_step(n, _ptrs(params), _ptrs(grads), _ptrs(exp_avg), _ptrs(exp_avg_sq), numel,
+                                       dtype_code(dt), int(step), ctypes.c_float(lr), ctypes.c_float(b1),
+                                       ctypes.c_float(b2), ctypes.c_float(eps), ctypes.c_float(weight_decay),
+                                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                       ctypes.c_void_p(_stream_handle(stream))),
+          "dmuon_adamw_step")
+
+
+class AdamWStep:
+    """AdamW state for a fixed list of non-matrix parameters: float32 moments
+    (zeros), the step counter and a reusable workspace.  Each call runs one
+    dmuon_adamw_step on the gradients given at construction."""
+
+    def __init__(self, params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], lr: float = 1e-3,
+                 betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.01):
+        self.params, self.grads = list(params), list(grads)
+        self.exp_avg = [torch.zeros(p.shape, dtype=torch.float32, device=p.device) for p in self.params]
+        self.exp_avg_sq = [torch.zeros(p.shape, dtype=torch.float32, device=p.device) for p in self.params]
+        self.lr, self.betas, self.eps, self.weight_decay = lr, tuple(betas), eps, weight_decay
+        self.step = 0
+        dev = self.params[0].device if self.params else None
+        self.workspace = alloc_workspace(adamw_step_workspace_bytes([p.numel() for p in self.params]), dev)
+
+    def __call__(self, stream=None) -> None:
+        self.step += 1
+        adamw_step_(self.params, self.grads, self.exp_avg, self.exp_avg_sq, self.step, self.lr, self.betas,
+                    self.eps, self.weight_decay, self.workspace, stream)
+
+
 def backend_info() -> str:
     return _lib.load().dmuon_backend_info().decode()
 

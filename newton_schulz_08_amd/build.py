@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libdmuon.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["kernels_elementwise.hip", "kernels_mfma.hip", "kernels_clip.hip", "dmuon_api.cpp"]
+SOURCES = ["kernels_elementwise.hip", "kernels_mfma.hip", "kernels_clip.hip", "kernels_adamw.hip", "dmuon_api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

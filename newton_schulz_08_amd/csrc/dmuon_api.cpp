@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "../../include/dmuon.h"
+#include "adamw.hpp"
 #include "clip.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -246,9 +247,9 @@ int check_device() {
 }
 
 // ---------------------------------------------------------------- profiler
-enum KernelClass { kKPrologue = 0, kKNorm, kKSyrk, kKGemm, kKApply, kKSquare, kKClip, kKNumClasses };
+enum KernelClass { kKPrologue = 0, kKNorm, kKSyrk, kKGemm, kKApply, kKSquare, kKClip, kKAdamw, kKNumClasses };
 const char* kClassNames[kKNumClasses] = {"prologue", "norm_finalize", "syrk", "ns_gemm", "apply_x0",
-                                         "syrk_square", "grad_clip"};
+                                         "syrk_square", "grad_clip",     "adamw"};
 
 struct ProfRecord {
   int cls;
@@ -590,6 +591,42 @@ ClipPlan make_clip_plan(int count, const int64_t* numel, const int* segment, int
   return cp;
 }
 
+// ---------------------------------------------------------------- AdamW
+struct AdamPlan {
+  std::vector<int> tile_prefix;  // size n + 1
+  size_t off_descs = 0, off_prefix = 0, total = 0;
+};
+
+int validate_adamw(int count, const int64_t* numel) {
+  if (count < 0) return fail(DMUON_ERR_INVALID_ARG, "count < 0");
+  if (count > 0 && !numel) return fail(DMUON_ERR_INVALID_ARG, "numel array is NULL");
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    if (numel[i] < 0) return fail(DMUON_ERR_INVALID_ARG, "numel[" + std::to_string(i) + "] < 0");
+    tiles += (numel[i] + kAdamTile - 1) / kAdamTile;
+    if (tiles > (int64_t{1} << 30)) return fail(DMUON_ERR_INVALID_ARG, "too many elements in one call");
+  }
+  return DMUON_OK;
+}
+
+AdamPlan make_adamw_plan(int count, const int64_t* numel) {
+  AdamPlan ap;
+  ap.tile_prefix.assign(count + 1, 0);
+  int t = 0;
+  for (int i = 0; i < count; ++i) {
+    ap.tile_prefix[i] = t;
+    t += static_cast<int>((numel[i] + kAdamTile - 1) / kAdamTile);
+  }
+  ap.tile_prefix[count] = t;
+  size_t off = 0;
+  ap.off_descs = off;
+  off = align_up(off + sizeof(AdamDesc) * std::max(count, 1));
+  ap.off_prefix = off;
+  off = align_up(off + sizeof(int) * (count + 1));
+  ap.total = off;
+  return ap;
+}
+
 int ws_check(const Plan& pl, void* workspace, size_t bytes) {
   if (!workspace) return fail(DMUON_ERR_WORKSPACE, "workspace is NULL");
   if (bytes < pl.total)
@@ -795,6 +832,98 @@ int dmuon_clip_grad_norm(int count, void* const* grads, const int64_t* numel, in
                        d_coef, totals_out, grid, stream);
   });
   if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("clip launch: ") + hipGetErrorString(e));
+  return DMUON_OK;
+}
+
+int dmuon_adamw_step_workspace_bytes(int count, const int64_t* numel, size_t* bytes_out) {
+  g_last_error.clear();
+  if (!bytes_out) return fail(DMUON_ERR_INVALID_ARG, "bytes_out is NULL");
+  int st = validate_adamw(count, numel);
+  if (st != DMUON_OK) return st;
+  *bytes_out = count == 0 ? 0 : make_adamw_plan(count, numel).total;
+  return DMUON_OK;
+}
+
+int dmuon_adamw_step(int count, void* const* params, const void* const* grads, float* const* exp_avg,
+                     float* const* exp_avg_sq, const int64_t* numel, int dtype, int step, float lr, float beta1,
+                     float beta2, float eps, float weight_decay, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+  g_last_error.clear();
+  int st = validate_adamw(count, numel);
+  if (st != DMUON_OK) return st;
+  if (dtype != kF32 && dtype != kBF16)
+    return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "dtype must be DMUON_F32 or DMUON_BF16");
+  if (step < 1) return fail(DMUON_ERR_INVALID_ARG, "step counts from 1");
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(eps) || eps < 0.0f)
+    return fail(DMUON_ERR_INVALID_ARG, "lr and weight_decay must be finite, eps finite and >= 0");
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(DMUON_ERR_INVALID_ARG, "betas must lie in [0, 1)");
+  if (count == 0) return DMUON_OK;
+  if (!params || !grads || !exp_avg || !exp_avg_sq) return fail(DMUON_ERR_INVALID_ARG, "a pointer array is NULL");
+  const size_t eb = elem_bytes(dtype);
+  std::vector<std::pair<const void*, std::string>> ptrs;
+  for (int i = 0; i < count; ++i) {
+    if (numel[i] == 0) continue;
+    const std::string s = "[" + std::to_string(i) + "]";
+    if (!params[i] || !grads[i] || !exp_avg[i] || !exp_avg_sq[i])
+      return fail(DMUON_ERR_INVALID_ARG, "a pointer of tensor " + s + " is NULL");
+    if (!aligned(params[i], eb) || !aligned(grads[i], eb) || !aligned(exp_avg[i], 4) || !aligned(exp_avg_sq[i], 4))
+      return fail(DMUON_ERR_INVALID_ARG, "tensor " + s + " is not aligned to its element size");
+    ptrs.push_back({params[i], "params" + s});
+    ptrs.push_back({grads[i], "grads" + s});
+    ptrs.push_back({exp_avg[i], "exp_avg" + s});
+    ptrs.push_back({exp_avg_sq[i], "exp_avg_sq" + s});
+  }
+  if ((st = check_distinct(ptrs)) != DMUON_OK) return st;
+  const AdamPlan ap = make_adamw_plan(count, numel);
+  if (!workspace) return fail(DMUON_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < ap.total)
+    return fail(DMUON_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                         std::to_string(ap.total));
+  if (!aligned(workspace, kAlign)) return fail(DMUON_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((st = check_device()) != DMUON_OK) return st;
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  std::vector<AdamDesc> descs(count);
+  double bytes = 0.0;
+  const size_t chunk_bytes = eb * kAdamChunk;
+  for (int i = 0; i < count; ++i) {
+    AdamDesc& d = descs[i];
+    std::memset(&d, 0, sizeof(d));
+    d.p = params[i];
+    d.g = grads[i];
+    d.m = exp_avg[i];
+    d.v = exp_avg_sq[i];
+    d.numel = numel[i];
+    d.vec_ok = aligned(params[i], chunk_bytes) && aligned(grads[i], chunk_bytes) && aligned(exp_avg[i], 16) &&
+               aligned(exp_avg_sq[i], 16);
+    // read p, g, m, v; write p, m, v
+    bytes += static_cast<double>(numel[i]) * (3.0 * eb + 16.0);
+  }
+  // bias corrections and the decay factor in double, each rounded once
+  const double t = static_cast<double>(step);
+  AdamArgs a{};
+  a.decay = static_cast<float>(1.0 - static_cast<double>(lr) * static_cast<double>(weight_decay));
+  a.beta1 = beta1;
+  a.one_minus_beta1 = static_cast<float>(1.0 - static_cast<double>(beta1));
+  a.beta2 = beta2;
+  a.one_minus_beta2 = static_cast<float>(1.0 - static_cast<double>(beta2));
+  a.step_size = static_cast<float>(static_cast<double>(lr) / (1.0 - std::pow(static_cast<double>(beta1), t)));
+  a.inv_bc2_sqrt = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(static_cast<double>(beta2), t)));
+  a.eps = eps;
+  AdamDesc* d_descs = reinterpret_cast<AdamDesc*>(ws + ap.off_descs);
+  int* d_prefix = reinterpret_cast<int*>(ws + ap.off_prefix);
+  if (hipMemcpyAsync(d_descs, descs.data(), sizeof(AdamDesc) * count, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(d_prefix, ap.tile_prefix.data(), sizeof(int) * (count + 1), hipMemcpyHostToDevice, stream) !=
+          hipSuccess)
+    return fail(DMUON_ERR_HIP, std::string("AdamW descriptor upload failed: ") + hipGetErrorString(hipGetLastError()));
+  const int tiles = ap.tile_prefix[count];
+  const int grid = std::max(1, std::min(tiles, 256 * 8));
+  hipError_t e = timed(kKAdamw, 0.0, bytes, stream, [&] {
+    return launch_adamw(dtype, d_descs, d_prefix, count, tiles, a, grid, stream);
+  });
+  if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("AdamW launch: ") + hipGetErrorString(e));
   return DMUON_OK;
 }
 

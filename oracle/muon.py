@@ -240,7 +240,9 @@ def adamw_step(p, g, m, v, step: int, lr: float, beta1: float, beta2: float, eps
                weight_decay: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """One AdamW step for a non-matrix parameter (training guide: group 1,
     "AdamW — 标准", with ``adamw_lr``, ``adamw_betas``, ``adamw_eps`` and
-    ``adamw_weight_decay``).  "Standard" is read as PyTorch's AdamW:
+    ``adamw_weight_decay``; blog post, section "为什么需要矩阵感知优化器",
+    whose update subtracts alpha m_hat / (sqrt(v_hat) + eps) with
+    bias-corrected moments).  "Standard" is read as PyTorch's AdamW:
 
         p <- p (1 - lr wd)
         m <- beta1 m + (1 - beta1) g

@@ -225,3 +225,46 @@ def test_clip_workspace_and_validation(lib):
     assert "alias" in _lib.last_error()
     assert call() == E.DMUON_ERR_WORKSPACE
     assert call(ws=0x100010) == E.DMUON_ERR_WORKSPACE
+
+
+def test_adamw_workspace_and_validation(lib):
+    E = _lib
+    n = (ctypes.c_int64 * 3)(4096, 10, 0)
+    out = ctypes.c_size_t(0)
+    assert lib.dmuon_adamw_step_workspace_bytes(3, n, ctypes.byref(out)) == 0
+    assert out.value == 2 * 256       # descriptors (3 x 48 B) and the tile prefix, 256-aligned regions
+    assert lib.dmuon_adamw_step_workspace_bytes(0, None, ctypes.byref(out)) == 0 and out.value == 0
+    bad = (ctypes.c_int64 * 1)(-1)
+    assert lib.dmuon_adamw_step_workspace_bytes(1, bad, ctypes.byref(out)) == E.DMUON_ERR_INVALID_ARG
+    P = (ctypes.c_void_p * 2)
+    nn = (ctypes.c_int64 * 2)(8, 8)
+
+    def call(p=P(0x1000, 0x2000), g=P(0x3000, 0x4000), m=P(0x5000, 0x6000), v=P(0x7000, 0x8000), dt=0, step=1,
+             lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.01, ws=None, wsb=1 << 20, numel=nn):
+        return lib.dmuon_adamw_step(2, p, g, m, v, numel, dt, step, ctypes.c_float(lr), ctypes.c_float(b1),
+                                    ctypes.c_float(b2), ctypes.c_float(eps), ctypes.c_float(wd), ws, wsb, None)
+
+    assert call(dt=5) == E.DMUON_ERR_UNSUPPORTED_DTYPE
+    assert call(step=0) == E.DMUON_ERR_INVALID_ARG
+    assert call(lr=float("nan")) == E.DMUON_ERR_INVALID_ARG
+    assert call(wd=float("inf")) == E.DMUON_ERR_INVALID_ARG
+    assert call(eps=-1.0) == E.DMUON_ERR_INVALID_ARG
+    assert call(b1=1.0) == E.DMUON_ERR_INVALID_ARG
+    assert call(b2=-0.5) == E.DMUON_ERR_INVALID_ARG
+    assert call(b2=float("nan")) == E.DMUON_ERR_INVALID_ARG
+    assert call(p=P(0, 0x2000)) == E.DMUON_ERR_INVALID_ARG
+    assert "NULL" in _lib.last_error()
+    assert call(m=P(0x5000, 0x3000)) == E.DMUON_ERR_INVALID_ARG
+    assert "alias" in _lib.last_error()
+    assert call(p=P(0x1001, 0x2000)) == E.DMUON_ERR_INVALID_ARG
+    assert "aligned" in _lib.last_error()
+    assert call(p=P(0x1002, 0x2000), g=P(0x3002, 0x4000), dt=_lib.DMUON_BF16) == E.DMUON_ERR_WORKSPACE
+    # an empty tensor's pointers are not looked at
+    assert call(p=P(0, 0x2000), g=P(0, 0x4000), numel=(ctypes.c_int64 * 2)(0, 8)) == E.DMUON_ERR_WORKSPACE
+    assert call() == E.DMUON_ERR_WORKSPACE
+    assert call(ws=0x100010) == E.DMUON_ERR_WORKSPACE
+    assert lib.dmuon_adamw_step(0, None, None, None, None, None, 0, 1, ctypes.c_float(1e-3), ctypes.c_float(0.9),
+                                ctypes.c_float(0.999), ctypes.c_float(1e-8), ctypes.c_float(0.0), None, 0,
+                                None) == E.DMUON_OK
+    if torch.cuda.device_count() == 0:
+        assert call(ws=0x10000000) == E.DMUON_ERR_NO_DEVICE
