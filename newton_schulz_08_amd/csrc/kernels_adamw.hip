@@ -12,8 +12,9 @@
 //   v <- beta2 v + (1 - beta2) g^2
 //   p <- p - step_size m / (sqrt(v) / sqrt(1 - beta2^t) + eps),   step_size = lr / (1 - beta1^t)
 //
-// One launch covers every tensor: tensors are cut into 4096-element tiles and
-// blocks stride over the tile list.  Each lane handles four consecutive
+// One launch covers every tensor: tensors are cut into 4096-element tiles, one
+// block per tile (blocks stride over the list only past 2^22 tiles), so the
+// dispatcher keeps every CU full to the end.  Each lane handles four consecutive
 // elements per load, so one wave instruction covers 256 consecutive elements
 // of every array (512 B of bf16, 1 KB of fp32): every access is fully
 // coalesced.  All loads of a tile are issued before any arithmetic.  Bytes per
@@ -71,6 +72,8 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(const AdamDesc* __r
         rm[c] = *reinterpret_cast<gptr<const f32v4>>(gmem(d.m + e));
         rv[c] = *reinterpret_cast<gptr<const f32v4>>(gmem(d.v + e));
       }
+      // keep every load of the tile ahead of the arithmetic
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < kAdamChunks; ++c) {
         const int64_t e = base + (c * kAdamThreads + threadIdx.x) * kAdamChunk;
