@@ -29,16 +29,17 @@ enum PrologueMode : int {
   kModeNsOnly = 1, // Y = x (dmuon_ns_batched)
 };
 
-// One matrix of the call.  Lives in the workspace; 144 bytes.
+// One matrix of the call.  Lives in the workspace; 128 bytes.
 struct alignas(16) MatDesc {
   const void* g;     // grad (muon step) or x_in (ns only)
   float* buf;        // momentum buffer (muon step) or nullptr
   void* p;           // params (muon step) or x_out (ns only)
   float* upd;        // optional fp32 update output (original orientation)
-  float* xm;         // workspace: fp32 iterate, Mp x Np
-  void* xs;          // workspace: Gram operand, Mp x Np (== xm for fp32)
-  void* xt0;         // workspace: transposed iterate, Np x Mp (even steps)
-  void* xt1;         // workspace: transposed iterate, Np x Mp (odd steps)
+  float* xm;         // workspace: fp32 iterate X, Mp x Np, updated in place (bf16: its own
+                     // buffer; fp32: the same memory as xs0)
+  void* xs0;         // workspace: operand copy of X (dtype), Mp x Np, read on even steps
+  void* xs1;         // workspace: operand copy of X, Mp x Np, read on odd steps (fp32: the
+                     // iterate itself alternates between xs0 and xs1)
   void* a;           // workspace: Gram matrix, Mp x Mp
   void* b;           // workspace: c1 A + c2 A^2 for three-term maps, Mp x Mp (else nullptr)
   int m, n;          // caller shape (rows, cols)
@@ -54,7 +55,7 @@ struct alignas(16) MatDesc {
   float lr_scale;
   float pad_;
 };
-static_assert(sizeof(MatDesc) == 144, "MatDesc layout");
+static_assert(sizeof(MatDesc) == 128, "MatDesc layout");
 
 // A run of equally shaped Newton-Schulz matrices inside one contraction launch.
 struct alignas(16) Segment {

@@ -47,7 +47,7 @@ struct MatPlan {
   bool ns, tr;
   int64_t mp, np;     // padded wide dims
   int ew_rows, ew_cols, ew_tiles;
-  size_t off_xm, off_xs, off_xt0, off_xt1, off_a, off_b;
+  size_t off_xm, off_xs0, off_xs1, off_a, off_b;
 };
 
 // Resolved Newton-Schulz configuration (dmuon_ns_config).
@@ -193,18 +193,17 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
   for (int k = 0; k < pl.n_ns; ++k) {
     MatPlan& mp = pl.mats[k];
     const size_t wide = static_cast<size_t>(mp.mp) * mp.np;
-    mp.off_xm = off;
-    off = align_up(off + 4 * wide);
+    // bf16: fp32 iterate + two bf16 operand copies; fp32: the iterate itself
+    // alternates between two buffers (the update reads one, writes the other)
     if (dt == kBF16) {
-      mp.off_xs = off;
-      off = align_up(off + eb * wide);
-    } else {
-      mp.off_xs = mp.off_xm;
+      mp.off_xm = off;
+      off = align_up(off + 4 * wide);
     }
-    mp.off_xt0 = off;
+    mp.off_xs0 = off;
     off = align_up(off + eb * wide);
-    mp.off_xt1 = off;
+    mp.off_xs1 = off;
     off = align_up(off + eb * wide);
+    if (dt != kBF16) mp.off_xm = mp.off_xs0;
     mp.off_a = off;
     off = align_up(off + eb * static_cast<size_t>(mp.mp) * mp.mp);
     mp.off_b = 0;
@@ -338,9 +337,8 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     d.upd = call.upd ? call.upd[i] : nullptr;
     if (mp.ns) {
       d.xm = reinterpret_cast<float*>(ws + mp.off_xm);
-      d.xs = ws + mp.off_xs;
-      d.xt0 = ws + mp.off_xt0;
-      d.xt1 = ws + mp.off_xt1;
+      d.xs0 = ws + mp.off_xs0;
+      d.xs1 = ws + mp.off_xs1;
       d.a = ws + mp.off_a;
       d.b = call.ns.terms == 3 ? ws + mp.off_b : nullptr;
       d.mp = static_cast<int>(mp.mp);
@@ -483,8 +481,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     const std::array<float, 3>& c = call.ns.coeffs[step];
     for (const auto& L : syrk_launches) {
       e = timed(kKSyrk, L.second.second, 0.0, stream, [&] {
-        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step == 0 ? 1 : 0, 0, 0.0f, 0.0f,
-                           stream);
+        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 0, 0.0f, 0.0f, stream);
       });
       if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk launch: ") + hipGetErrorString(e));
     }
@@ -495,7 +492,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
       // B = c2 A A + c1 A
       for (const auto& L : square_launches) {
         e = timed(kKSquare, L.second.second, 0.0, stream, [&] {
-          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, 0, 1, c[2], c[1], stream);
+          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 1, c[2], c[1], stream);
         });
         if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk square launch: ") + hipGetErrorString(e));
       }

@@ -7,10 +7,11 @@
 //   small matrices (numel < 100000, training guide "编写 Predicate"):
 //     p <- p (1 - lr wd) - lr * s * Y, update_out <- Y  (blog VanillaMuon non-matrix
 //     branch, with the decoupled weight decay of the training guide's optimizer)
-//   Newton-Schulz matrices: Y is written, unnormalised, as the fp32 iterate, its
-//   operand copy and its transpose in the wide orientation (the transposed
-//   stores go through an LDS tile so both sides stay coalesced).  The 1/||Y||
-//   scale is folded into the first Newton-Schulz step instead of a second pass.
+//   Newton-Schulz matrices: Y is written, unnormalised, in the wide
+//   orientation as the fp32 iterate and (bf16) its operand copy; a tall
+//   matrix's tile goes through an LDS transpose so both sides stay coalesced.
+//   The 1/||Y|| scale is folded into the first Newton-Schulz step instead of a
+//   second pass.
 // norm_finalize_kernel -- fixed-order sum of each matrix's tile partials.
 // apply_x0_kernel -- ns_steps == 0 only: U = Y / (||Y|| + eps) to the caller.
 #include <hip/hip_runtime.h>
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
     const int r0 = tr_ * kEwTile, c0 = (local - tr_ * d.ew_tiles_c) * kEwTile;
     const int m = d.m, n = d.n;
     const bool ns = d.ns != 0, trn = d.tr != 0;
-    const int mp = d.mp, np = d.np;
+    const int np = d.np;
     const float step_lr = -lr * d.lr_scale;
     float ss = 0.0f;
 
@@ -147,18 +148,19 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
       if (ns) {
         // the covered extent is padded to 256, so every tile position exists
         if (!trn) {
+          // wide: caller rows are rows of X (fp32 iterate; bf16 operand copy)
           const long w = static_cast<long>(r) * np + c;
           store4(d.xm + w, true, 4, y);
-          if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs) + w, true, 4, y);
+          if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs0) + w, true, 4, y);
         } else {
-          store4(static_cast<T*>(d.xt0) + static_cast<long>(r) * mp + c, true, 4, y);
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tile[rl][cl + e] = y[e];
+          for (int e = 0; e < 4; ++e) tile[rl][cl + e] = y[e];
+        }
       }
     }
 
-    if (ns) {
+    if (ns && trn) {
+      // tall: caller columns are rows of X, written through the LDS tile
       __syncthreads();
 #pragma unroll
       for (int pass = 0; pass < 4; ++pass) {
@@ -166,13 +168,9 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = tile[cl + e][j];
-        if (!trn) {
-          store4(static_cast<T*>(d.xt0) + static_cast<long>(c0 + j) * mp + r0 + cl, true, 4, v);
-        } else {
-          const long w = static_cast<long>(c0 + j) * np + r0 + cl;
-          store4(d.xm + w, true, 4, v);
-          if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs) + w, true, 4, v);
-        }
+        const long w = static_cast<long>(c0 + j) * np + r0 + cl;
+        store4(d.xm + w, true, 4, v);
+        if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs0) + w, true, 4, v);
       }
     }
 

@@ -44,6 +44,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
 
 constexpr int kStageBytes = 65536;   // P (32 KB) + Q (32 KB)
 constexpr int kOperandBytes = 32768; // 256 rows x 128 bytes
@@ -156,18 +158,22 @@ struct WaveGrid {
   static constexpr int kLoadsPerOperand = 256 / kWaves / 8;  // 8-row wave loads per operand
 };
 
-// Accumulate the 256x256 tile of P * Q^T into acc.  P0/Q0 point at the first
-// row of each 256-row panel; ld*_bytes are row pitches; kbytes the contraction
-// length in bytes (a multiple of 128, at least 512).  after_last_barrier() runs
-// once every wave has read its last operand fragment: from then on the
-// caller owns all of the LDS, while the final MFMAs are still in flight.
+// Accumulate the 256x256 tile of P * Q^T into acc.  P0 points at the first
+// row of the 256-row P panel, rows K-contiguous, pitch ldp_bytes.  Q comes in
+// one of two layouts:
+//   QN == false: like P, 256 rows (j) with K contiguous (the Gram: rows of X);
+//   QN == true:  K rows of 256 columns (j) with j contiguous (the update: X
+//                itself); Q0 points at row 0, column j0, pitch ldq_bytes.
+// kbytes is the contraction length in bytes (a multiple of 128, at least
+// 512).  after_last_barrier() runs once every wave has read its last operand
+// fragment: from then on the caller owns all of the LDS, while the final
+// MFMAs are still in flight.
 //
 // Global -> LDS: global_load_lds_dwordx4 writes lane l's 16 bytes to
-// LDS[M0 + 16 l], so one wave instruction fills 8 rows x 128 bytes.  Each lane
+// LDS[M0 + 16 l], so one wave instruction fills 1 KB of a stage.  Each lane
 // fetches the source chunk that belongs in its slot of the XOR-swizzled
-// layout the fragment reads expect, so there is no VGPR staging.  Wave w
-// loads rows [w * 256 / kWaves, (w + 1) * 256 / kWaves) of both operands.
-template <int DT, int kWaves, typename AfterLastBarrier>
+// layout the fragment reads expect, so there is no VGPR staging.
+template <int DT, int kWaves, bool QN, typename AfterLastBarrier>
 __device__ __forceinline__ void block_product(const char* __restrict__ P0, int ldp_bytes,
                                               const char* __restrict__ Q0, int ldq_bytes, int kbytes, char* lds,
                                               f32x16 (&acc)[4][WaveGrid<kWaves>::kBN],
@@ -175,64 +181,122 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
   using G = WaveGrid<kWaves>;
   constexpr int kBN = G::kBN;
   constexpr int kRowsPerWave = 256 / kWaves;
+  constexpr int EB = (DT == kBF16) ? 2 : 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / G::kWN, wc = wave % G::kWN;
   const int li = lane & 31, lh = lane >> 5;
 
-  // Row r of a stage stores logical 16-byte chunk c at slot c ^ swz(r) with
-  // swz(r) = (r & 7) ^ ((r >> 3) & 1): the 16 lanes an LDS cycle serves for
-  // ds_read_b128 (rows r..r+15, 64 banks) and any 8 consecutive rows then hit
-  // distinct banks.  The wave's 8-row load groups start at multiples of 8, so
-  // for load group u the swizzle is lrow ^ (u & 1).
+  // K-contiguous operands: row r of a stage stores logical 16-byte chunk c at
+  // slot c ^ swz(r) with swz(r) = (r & 7) ^ ((r >> 3) & 1): the 16 lanes an
+  // LDS cycle serves for ds_read_b128 (rows r..r+15, 64 banks) and any 8
+  // consecutive rows then hit distinct banks.  The wave's 8-row load groups
+  // start at multiples of 8, so for load group u the swizzle is lrow ^ (u & 1).
   P0 = uniform_ptr(P0);
   Q0 = uniform_ptr(Q0);
   const int lrow = lane >> 3;                    // row within an 8-row group
   const int lchunk0 = (lane & 7) ^ lrow;         // source chunk, even load groups
   const int lchunk1 = lchunk0 ^ 1;               // odd load groups
   const uint32_t rp = static_cast<uint32_t>((wave * kRowsPerWave + lrow) * ldp_bytes);
-  const uint32_t rq = static_cast<uint32_t>((wave * kRowsPerWave + lrow) * ldq_bytes);
   const uint32_t offp0 = rp + lchunk0 * 16, offp1 = rp + lchunk1 * 16;
-  const uint32_t offq0 = rq + lchunk0 * 16, offq1 = rq + lchunk1 * 16;
-  const uint32_t grp_p = static_cast<uint32_t>(8 * ldp_bytes), grp_q = static_cast<uint32_t>(8 * ldq_bytes);
-  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * kRowsPerWave * 128);
+  const uint32_t grp_p = static_cast<uint32_t>(8 * ldp_bytes);
 
-  auto issue = [&](int stage, int kb) {
-    const uint32_t dp = lds_wave + stage * kStageBytes;
-#pragma unroll
-    for (int u = 0; u < G::kLoadsPerOperand; ++u) {
-      lds_dma16(P0, ((u & 1) ? offp1 : offp0) + u * grp_p + kb, dp + u * 1024);
-      lds_dma16(Q0, ((u & 1) ? offq1 : offq0) + u * grp_q + kb, dp + kOperandBytes + u * 1024);
-    }
-  };
+  // Q offsets.  K-contiguous: as P.  Column-contiguous (QN): a stage holds
+  // kQRows rows of 256 * EB bytes (64 bf16 / 32 fp32 rows, the same K as a
+  // 128-byte K step); wave w fills rows of KB blocks 4 w .. 4 w + 3.  Row r of
+  // the stage stores logical chunk c at slot c ^ qswz(r):
+  //   bf16: qswz(r) = 4 (r & 3)       -- ds_read_b64_tr_b16 reads rows r0..r0+3
+  //                                      (r0 % 4 == 0), 64 bytes each: distinct banks
+  //   fp32: qswz(r) = 8 ((r >> 2) & 1) -- 4-byte reads of rows r and r + 4,
+  //                                      128 bytes each: distinct banks
+  constexpr int kQRowBytes = 256 * EB;
+  constexpr int kQRows = kOperandBytes / kQRowBytes;   // K rows per stage
+  constexpr int kQRowsPerKB = 1024 / kQRowBytes;       // rows per 1 KB wave load
+  uint32_t offq0, offq1, grp_q;
+  if constexpr (QN) {
+    const int sub = lane / (64 / kQRowsPerKB);          // row within the KB block
+    const int pc = lane % (64 / kQRowsPerKB);           // physical chunk in the row
+    const int r0 = wave * 4 * kQRowsPerKB + sub;        // rows of load u: r0 + u * kQRowsPerKB
+    auto qswz = [](int r) { return (DT == kBF16) ? 4 * (r & 3) : 8 * ((r >> 2) & 1); };
+    offq0 = static_cast<uint32_t>(r0 * ldq_bytes + ((pc ^ qswz(r0)) << 4));
+    offq1 = static_cast<uint32_t>((r0 + kQRowsPerKB) * ldq_bytes + ((pc ^ qswz(r0 + kQRowsPerKB)) << 4)) -
+            static_cast<uint32_t>(kQRowsPerKB * ldq_bytes);
+    grp_q = static_cast<uint32_t>(kQRowsPerKB * ldq_bytes);
+  } else {
+    const uint32_t rq = static_cast<uint32_t>((wave * kRowsPerWave + lrow) * ldq_bytes);
+    offq0 = rq + lchunk0 * 16;
+    offq1 = rq + lchunk1 * 16;
+    grp_q = static_cast<uint32_t>(8 * ldq_bytes);
+  }
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * kRowsPerWave * 128);
 
   // fragment reads: row (block * 32 + li), logical chunk 2 s + lh
   const int frag_row = li * 128;
   const int sw = (li & 7) ^ ((li >> 3) & 1);
+  // QN fragment offsets (bytes within the Q region of a stage, without the
+  // sub-step's row offset), one per 32-column block x of the wave
+  int qfrag[kBN];
+  if constexpr (QN) {
+#pragma unroll
+    for (int x = 0; x < kBN; ++x) {
+      const int J = wc * kBN + x;
+      if constexpr (DT == kBF16) {
+        // transposed read r of sub-step s: lane reads row 16 s + 8 lh + 4 r + t,
+        // t = (lane >> 2) & 3, columns 32 J + 16 ((lane >> 4) & 1) + 4 (lane & 3) + 0..3
+        const int t = (lane >> 2) & 3;
+        qfrag[x] = (8 * lh + t) * kQRowBytes + ((4 * (J ^ t) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) << 4) +
+                   8 * (lane & 1);
+      } else {
+        // element e of sub-step s: row 8 s + 4 lh + e, column 32 J + li
+        qfrag[x] = 4 * lh * kQRowBytes + ((8 * (J ^ lh) + (li >> 2)) << 4) + 4 * (li & 3);
+      }
+    }
+  }
 
   using Frag = typename std::conditional<DT == kBF16, bf16x8, f32x4>::type;
   Frag fa[2][4], fb[2][kBN];
   constexpr int kMfma = 4 * kBN;                    // MFMA blocks per sub-step
   constexpr int kReads = 4 + kBN;                   // fragment reads per sub-step
   constexpr int kDma = 2 * G::kLoadsPerOperand;     // DMA loads per stage
+  auto read_q = [&](int stage, int s, int rs, int x) {
+    const char* qbase = lds + stage * kStageBytes + kOperandBytes;
+    if constexpr (!QN) {
+      const int co = (((2 * s + lh) ^ sw) << 4);
+      fb[rs][x] = *reinterpret_cast<const Frag*>(qbase + frag_row + co + (wc * kBN + x) * 32 * 128);
+    } else if constexpr (DT == kBF16) {
+      const char* b = qbase + qfrag[x] + 16 * s * kQRowBytes;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4_ptr>((lds_cptr_t)b));
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4_ptr>((lds_cptr_t)(b + 4 * kQRowBytes)));
+      fb[rs][x] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      const char* b = qbase + qfrag[x] + 8 * s * kQRowBytes;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fb[rs][x][e] = *reinterpret_cast<const float*>(b + e * kQRowBytes);
+    }
+  };
   // read i of a sub-step, in the order the MFMAs need them: fb[0], fa[0], fb[1..], fa[1..]
   auto read_one = [&](int stage, int s, int rs, int i) {
     const int co = (((2 * s + lh) ^ sw) << 4);
     const char* base = lds + stage * kStageBytes + frag_row + co;
-    int isb, x;
-    if (i == 0) { isb = 1; x = 0; }
-    else if (i == 1) { isb = 0; x = 0; }
-    else if (i < kBN + 1) { isb = 1; x = i - 1; }
-    else { isb = 0; x = i - kBN; }
-    if (isb) fb[rs][x] = *reinterpret_cast<const Frag*>(base + kOperandBytes + (wc * kBN + x) * 32 * 128);
-    else fa[rs][x] = *reinterpret_cast<const Frag*>(base + (wr * 4 + x) * 32 * 128);
+    if (i == 0) read_q(stage, s, rs, 0);
+    else if (i == 1) fa[rs][0] = *reinterpret_cast<const Frag*>(base + (wr * 4) * 32 * 128);
+    else if (i < kBN + 1) read_q(stage, s, rs, i - 1);
+    else fa[rs][i - kBN] = *reinterpret_cast<const Frag*>(base + (wr * 4 + i - kBN) * 32 * 128);
   };
+  // DMA load i of the stage starting at K byte offset kb (K-contiguous units)
   auto dma_one = [&](int stage, int kb, int i) {
     const uint32_t dp = lds_wave + stage * kStageBytes;
     const int u = i >> 1;
-    if ((i & 1) == 0) lds_dma16(P0, ((u & 1) ? offp1 : offp0) + u * grp_p + kb, dp + u * 1024);
-    else lds_dma16(Q0, ((u & 1) ? offq1 : offq0) + u * grp_q + kb, dp + kOperandBytes + u * 1024);
+    if ((i & 1) == 0) {
+      lds_dma16(P0, ((u & 1) ? offp1 : offp0) + u * grp_p + kb, dp + u * 1024);
+    } else if constexpr (QN) {
+      const char* qk = Q0 + static_cast<long>(kb >> 7) * kQRows * static_cast<long>(ldq_bytes);
+      lds_dma16(qk, ((u & 1) ? offq1 : offq0) + u * grp_q, dp + kOperandBytes + u * 1024);
+    } else {
+      lds_dma16(Q0, ((u & 1) ? offq1 : offq0) + u * grp_q + kb, dp + kOperandBytes + u * 1024);
+    }
   };
   auto mfma_one = [&](int rs, int j) {
     const int mi = j / kBN, ni = j % kBN;
@@ -430,7 +494,7 @@ __device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float s
 
 template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __restrict__ descs, SegTable st,
-                                                          const MatScale* __restrict__ scales, int first_step,
+                                                          const MatScale* __restrict__ scales, int step,
                                                           int square, float cq, float cl) {
   using T = typename Elem<DT>::T;
   constexpr int EB = Elem<DT>::kBytes;
@@ -441,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   const int mp = d.mp, np = d.np;
   // Gram of the iterate (K = Np), or the square of the symmetric Gram matrix
   // (K = Mp) for the c2 A^2 term of a three-term map
-  const char* xs = static_cast<const char*>(square ? d.a : d.xs);
+  const char* xs = static_cast<const char*>(square ? d.a : ((step & 1) ? d.xs1 : d.xs0));
   const int kdim = square ? mp : np;
   const long ld = static_cast<long>(kdim) * EB;
 
@@ -451,10 +515,10 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
 #pragma unroll
     for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
-  block_product<DT, kWaves>(xs + static_cast<long>(tr.bi) * kTile * ld, ld, xs + static_cast<long>(tr.bj) * kTile * ld,
-                            ld, kdim * EB, lds, acc, [] {});
+  block_product<DT, kWaves, false>(xs + static_cast<long>(tr.bi) * kTile * ld, ld,
+                                   xs + static_cast<long>(tr.bj) * kTile * ld, ld, kdim * EB, lds, acc, [] {});
 
-  const float alpha = square ? cq : (first_step ? scales[tr.mat].c2 : 1.0f);
+  const float alpha = square ? cq : (step == 0 ? scales[tr.mat].c2 : 1.0f);
   T* a = static_cast<T*>(square ? d.b : d.a);
   const T* a_in = static_cast<const T*>(d.a);
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
@@ -514,7 +578,9 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   const MatDesc& d = descs[tr.mat];
   const int mp = d.mp, np = d.np;
   const char* a = static_cast<const char*>(poly ? d.b : d.a);
-  const char* xt_in = static_cast<const char*>((step & 1) ? d.xt1 : d.xt0);
+  // X of this step (operand copy) and the copy the epilogue writes for the next
+  const char* xq = static_cast<const char*>((step & 1) ? d.xs1 : d.xs0);
+  T* xs_next = static_cast<T*>((step & 1) ? d.xs0 : d.xs1);
   const long lda = static_cast<long>(mp) * EB;
 
   f32x16 acc[4][kBN];
@@ -528,32 +594,33 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   const float gamma = (step == 0) ? scales[tr.mat].c : 1.0f;
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
   const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
-  float* xm = d.xm;
-  T* xs = static_cast<T*>(d.xs);
-  T* xt_out = static_cast<T*>((step & 1) ? d.xt0 : d.xt1);
+  // fp32 iterate: bf16 keeps it in place in xm; for fp32 the operand copies
+  // are the iterate, so it moves from xq to xs_next
+  const float* xold = (DT == kBF16) ? d.xm : reinterpret_cast<const float*>(xq);
+  float* xnew = (DT == kBF16) ? d.xm : reinterpret_cast<float*>(xs_next);
   const bool trn = d.tr != 0;
   const float step_lr = -lr * d.lr_scale;
   // The tile is finished in four 64-row quarters through two 64 KB LDS
   // buffers.  Quarter q's fp32 iterate rows arrive by LDS-DMA in the staging
   // layout, the waves holding its accumulators replace them in place by
-  // gamma (1.5 X - 0.5 A X), and then every wave stores rows and column
-  // segments from LDS.  Quarter q + 1's DMA is issued before quarter q's
-  // stores, so the wait for it (vmcnt counts loads and stores in issue order)
-  // leaves those stores in flight.
+  // gamma (1.5 X - 0.5 A X), and then every wave stores rows from LDS.
+  // Quarter q + 1's DMA is issued before quarter q's stores, so the wait for
+  // it (vmcnt counts loads and stores in issue order) leaves those stores in
+  // flight.
   constexpr int kQRows = 64;
   constexpr int kQBytes = kQRows * 1024;
   constexpr int kDmaRows = kQRows / (kThreads / 64);         // rows per wave per quarter
   constexpr int kRowIt = kQRows * 64 / kThreads;             // row chunks per thread per quarter
   constexpr int kColIt = 256 * (kQRows / 8) / kThreads;      // column segments per thread per quarter
   // store instructions per thread per quarter on a non-final step
-  constexpr int kStoresQ = (DT == kBF16) ? (2 * kRowIt + kColIt) : (kRowIt + 2 * kColIt);
+  constexpr int kStoresQ = (DT == kBF16) ? 2 * kRowIt : kRowIt;
   const int c = tid & 63, col = Ct + 4 * c;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, lh = lane >> 5;
   const int cbase = (wave % Grid::kWN) * kBN * 8;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
   auto dma_quarter = [&](int q) {
-    const char* xb = uniform_ptr(reinterpret_cast<const char*>(xm + static_cast<long>(Rt + kQRows * q) * np + Ct));
+    const char* xb = uniform_ptr(reinterpret_cast<const char*>(xold + static_cast<long>(Rt + kQRows * q) * np + Ct));
     const uint32_t dst = lds0 + (q & 1) * kQBytes;
 #pragma unroll
     for (int i = 0; i < kDmaRows; ++i) {
@@ -562,8 +629,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
       lds_dma16(xb, voff, dst + r * 1024);
     }
   };
-  block_product<DT, kWaves>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
-                            xt_in + static_cast<long>(tr.bj) * kTile * lda, lda, mp * EB, lds, acc, [&] {
+  block_product<DT, kWaves, true>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
+                                  xq + static_cast<long>(tr.bj) * kTile * EB, np * EB, mp * EB, lds, acc, [&] {
     dma_quarter(0);
     dma_quarter(1);
   });
@@ -597,8 +664,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
     }
     __syncthreads();
     if (!last) {
-      // iterate rows (fp32 and its bf16 copy) and 8-row column segments of the
-      // transposed copy, in batches: LDS reads first, then the stores
+      // iterate rows: fp32 and (bf16) the next step's operand copy, in
+      // batches of four rows, LDS reads first, then the stores
 #pragma unroll
       for (int kb = 0; kb < kRowIt; kb += 4) {
         f32v4 rv[4];
@@ -611,22 +678,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
         for (int k = 0; k < 4; ++k) {
           const int row = Rt + kQRows * q + (tid >> 6) + (kThreads / 64) * (kb + k);
           const float xn[4] = {rv[k].x, rv[k].y, rv[k].z, rv[k].w};
-          vst4(xm + static_cast<long>(row) * np + col, xn);
-          if constexpr (DT == kBF16) vst4(xs + static_cast<long>(row) * np + col, xn);
-        }
-      }
-#pragma unroll
-      for (int jb = 0; jb < kColIt; jb += 2) {
-        float cv[2][8];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int qq = tid + kThreads * (jb + j);
-          stage_col8(buf, qq & 7, qq >> 3, cv[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int qq = tid + kThreads * (jb + j);
-          vst8(xt_out + static_cast<long>(Ct + (qq >> 3)) * mp + Rt + kQRows * q + 8 * (qq & 7), cv[j]);
+          vst4(xnew + static_cast<long>(row) * np + col, xn);
+          if constexpr (DT == kBF16) vst4(xs_next + static_cast<long>(row) * np + col, xn);
         }
       }
     } else if (!trn) {
@@ -660,13 +713,13 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
 }  // namespace
 
 hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                       int first_step, int square, float cq, float cl, hipStream_t stream) {
+                       int step, int square, float cq, float cl, hipStream_t stream) {
   if (ntiles <= 0) return hipSuccess;
   if (dt == kBF16)
-    hipLaunchKernelGGL(syrk_kernel<kBF16>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, first_step,
+    hipLaunchKernelGGL(syrk_kernel<kBF16>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, step,
                        square, cq, cl);
   else
-    hipLaunchKernelGGL(syrk_kernel<kF32>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, first_step,
+    hipLaunchKernelGGL(syrk_kernel<kF32>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, step,
                        square, cq, cl);
   return hipGetLastError();
 }

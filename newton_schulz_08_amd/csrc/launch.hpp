@@ -31,14 +31,17 @@ hipError_t launch_norm_finalize(const MatDesc* descs, const int* tile_prefix, in
 hipError_t launch_apply_x0(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
                            const MatScale* scales, int mode, float lr, float decay, int grid, hipStream_t stream);
 
-// Gram products over a launch's segments.
-//   square == 0: A = alpha X X^T (alpha = c^2 at the first step, else 1).
+// Gram products over a launch's segments, for Newton-Schulz step `step`.
+//   square == 0: A = alpha X X^T (alpha = c^2 at step 0, else 1), X read from
+//                the operand copy of that step (xs0 on even steps, xs1 on odd).
 //   square == 1: B = cq A A + cl A (A symmetric, so A A = A A^T).
 hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                       int first_step, int square, float cq, float cl, hipStream_t stream);
+                       int step, int square, float cq, float cl, hipStream_t stream);
 
 // X <- g (cx X + cax M X) with M = A (poly == 0) or B (poly == 1); g = c at
-// step 0, else 1.  On the last step the result U is written to the caller:
+// step 0, else 1.  The product reads the operand copy of step `step` and the
+// epilogue writes the next step's copy (and, for bf16, the fp32 iterate in
+// place).  On the last step the result U is written to the caller:
 // p <- p * decay + step_lr * U (mode muon) or out = U (ns only).
 hipError_t launch_ns_gemm(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
                           int step, int last, int mode, float lr, float decay, float cx, float cax, int poly,

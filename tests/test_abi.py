@@ -74,16 +74,16 @@ def _cfg(backend=0, terms=0, per_step=0, coeffs=()):
 
 
 def test_workspace_layout_exact(lib):
-    # one 512x2048 fp32 matrix: descriptor 144 B, prefix 8 B, 256 prologue
+    # one 512x2048 fp32 matrix: descriptor 128 B, prefix 8 B, 256 prologue
     # tiles (1 KB), scales 16 B -- each region 256-aligned -- then the fp32
-    # iterate (aliased as the Gram operand), two transposed copies and A
+    # iterate in two buffers that alternate between steps, and A
     st, nbytes = _ws(lib, [(512, 2048)], dt=0)
     assert st == 0
     mb = 512 * 2048 * 4
-    assert nbytes == 256 + 256 + 1024 + 256 + 3 * mb + 512 * 512 * 4
-    # bf16: fp32 iterate + bf16 operand + 2 bf16 transposed + bf16 Gram
+    assert nbytes == 256 + 256 + 1024 + 256 + 2 * mb + 512 * 512 * 4
+    # bf16: fp32 iterate + two bf16 operand copies + bf16 Gram
     st, nb16 = _ws(lib, [(512, 2048)], dt=1)
-    assert nb16 == 256 + 256 + 1024 + 256 + 512 * 2048 * (4 + 2 + 2 + 2) + 512 * 512 * 2
+    assert nb16 == 256 + 256 + 1024 + 256 + 512 * 2048 * (4 + 2 + 2) + 512 * 512 * 2
     # a three-term polynomial adds the m' x m' buffer B = c1 A + c2 A^2
     st, nb3 = _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(terms=3, coeffs=(3.4445, -4.775, 2.0315)))
     assert st == 0 and nb3 == nb16 + 512 * 512 * 2
