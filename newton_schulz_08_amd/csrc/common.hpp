@@ -17,7 +17,9 @@
 namespace dmuon {
 
 constexpr int kTile = 256;           // MFMA block tile (rows and cols)
-constexpr int kEwTile = 64;          // elementwise / transpose tile
+constexpr int kEwTile = 64;          // elementwise tile of a transposed (tall) matrix: 64 x 64
+constexpr int kEwRowTileRows = 16;   // elementwise tile of every other matrix: 16 x 256
+constexpr int kEwRowTileCols = 256;
 constexpr int kEwThreads = 256;
 constexpr float kNormEps = 1e-7f;    // blog post: G / (G.norm() + 1e-7)
 

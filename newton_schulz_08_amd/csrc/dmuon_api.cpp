@@ -118,6 +118,11 @@ struct Plan {
 
 size_t elem_bytes(int dt) { return dt == kBF16 ? 2 : 4; }
 
+// Elementwise tile shape of a matrix: 64 x 64 for a tall Newton-Schulz matrix
+// (written transposed through LDS), 16 x 256 otherwise.
+int ew_tile_rows(const MatPlan& mp) { return (mp.ns && mp.tr) ? kEwTile : kEwRowTileRows; }
+int ew_tile_cols(const MatPlan& mp) { return (mp.ns && mp.tr) ? kEwTile : kEwRowTileCols; }
+
 int validate_shapes(int count, const int64_t* rows, const int64_t* cols, int dt) {
   if (count < 0) return fail(DMUON_ERR_INVALID_ARG, "count < 0");
   if (dt != kF32 && dt != kBF16) return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "dtype must be DMUON_F32 or DMUON_BF16");
@@ -153,8 +158,8 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
       mp.ew_cols = static_cast<int>(mp.tr ? mp.mp : mp.np);
       ns_mats.push_back(mp);
     } else {
-      mp.ew_rows = static_cast<int>(round_up(mp.m, kEwTile));
-      mp.ew_cols = static_cast<int>(round_up(mp.n, kEwTile));
+      mp.ew_rows = static_cast<int>(round_up(mp.m, kEwRowTileRows));
+      mp.ew_cols = static_cast<int>(round_up(mp.n, kEwRowTileCols));
       ew_mats.push_back(mp);
     }
   }
@@ -175,7 +180,7 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
 
   int tiles = 0;
   for (auto& mp : pl.mats) {
-    mp.ew_tiles = (mp.ew_rows / kEwTile) * (mp.ew_cols / kEwTile);
+    mp.ew_tiles = (mp.ew_rows / ew_tile_rows(mp)) * (mp.ew_cols / ew_tile_cols(mp));
     tiles += mp.ew_tiles;
   }
   pl.total_tiles = tiles;
@@ -350,7 +355,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     d.ns = mp.ns ? 1 : 0;
     d.out_index = i;
     d.ew_tile0 = tile0;
-    d.ew_tiles_c = mp.ew_cols / kEwTile;
+    d.ew_tiles_c = mp.ew_cols / ew_tile_cols(mp);
     d.ew_rows = mp.ew_rows;
     d.ew_cols = mp.ew_cols;
     const size_t va = 4 * eb;  // 4 elements of dtype
@@ -389,7 +394,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     pro_bytes += b;
   }
 
-  const int ew_grid = std::min(pl.total_tiles, 256 * 8);
+  const int ew_grid = std::min(pl.total_tiles, 1 << 22);   // one block per tile
   hipError_t e = timed(kKPrologue, 0.0, pro_bytes, stream, [&] {
     return launch_prologue(dt, d_descs, d_prefix, pl.count, pl.total_tiles, d_partials, call.mode, call.mu,
                            call.nesterov, call.lr, call.decay, ew_grid, stream);

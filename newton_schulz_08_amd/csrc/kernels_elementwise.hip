@@ -82,6 +82,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Tile shapes (4096 elements, 256 threads, four passes of four elements per
+// thread).  A tall Newton-Schulz matrix is written transposed, so its tiles
+// are 64 x 64 and go through LDS; every other matrix uses 16 x 256 tiles, in
+// which one wave instruction covers 256 consecutive elements of one row.
+struct EwShape {
+  int rows, cols, tpr;  // tile rows, tile cols, threads per row
+};
+__device__ __forceinline__ EwShape ew_shape(bool transposed) {
+  return transposed ? EwShape{kEwTile, kEwTile, kEwTile / 4} : EwShape{kEwRowTileRows, kEwRowTileCols, kEwRowTileCols / 4};
+}
+
 template <int DT>
 __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __restrict__ descs,
                                                               const int* __restrict__ prefix, int nmat,
@@ -92,55 +103,65 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
   __shared__ float tile[kEwTile][kEwTile + 1];
   __shared__ float red[kEwThreads / 64];
   const int tid = threadIdx.x;
-  const int cl = (tid & 15) * 4;  // 4 consecutive columns
-  const int rl0 = tid >> 4;       // rows rl0 + 16 * pass
 
   for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
     const MatDesc& d = descs[find_matrix(prefix, nmat, t)];
-    const int local = t - d.ew_tile0;
-    const int tr_ = local / d.ew_tiles_c;
-    const int r0 = tr_ * kEwTile, c0 = (local - tr_ * d.ew_tiles_c) * kEwTile;
     const int m = d.m, n = d.n;
     const bool ns = d.ns != 0, trn = d.tr != 0;
+    const EwShape sh = ew_shape(ns && trn);
+    const int local = t - d.ew_tile0;
+    const int tr_ = local / d.ew_tiles_c;
+    const int r0 = tr_ * sh.rows, c0 = (local - tr_ * d.ew_tiles_c) * sh.cols;
+    const int cl = (tid % sh.tpr) * 4;   // 4 consecutive columns
+    const int rl0 = tid / sh.tpr;        // rows rl0 + rstep * pass
+    const int rstep = kEwThreads / sh.tpr;
     const int np = d.np;
     const float step_lr = -lr * d.lr_scale;
     float ss = 0.0f;
 
+    // every load of the tile first, then the arithmetic and the stores
+    float g[4][4], b[4][4], pv[4][4];
+    bool in[4], vec[4];
+    int valid[4];
+    long o[4];
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
-      const int rl = rl0 + 16 * pass;
+      const int r = r0 + rl0 + rstep * pass, c = c0 + cl;
+      in[pass] = r < m && c < n;
+      valid[pass] = in[pass] ? min(4, n - c) : 0;
+      vec[pass] = d.vec_ok && valid[pass] == 4;
+      o[pass] = static_cast<long>(r) * n + c;
+      if (in[pass]) {
+        load4(static_cast<const T*>(d.g) + o[pass], vec[pass], valid[pass], g[pass]);
+        if (mode == kModeMuon) load4(d.buf + o[pass], vec[pass], valid[pass], b[pass]);
+        if (!ns) load4(static_cast<const T*>(d.p) + o[pass], vec[pass], valid[pass], pv[pass]);
+      }
+    }
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rl = rl0 + rstep * pass;
       const int r = r0 + rl, c = c0 + cl;
       float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (r < m && c < n) {
-        const int valid = min(4, n - c);
-        const bool vec = d.vec_ok && valid == 4;
-        const long o = static_cast<long>(r) * n + c;
-        float g[4];
-        load4(static_cast<const T*>(d.g) + o, vec, valid, g);
+      if (in[pass]) {
         if (mode == kModeMuon) {
-          float b[4];
-          load4(d.buf + o, vec, valid, b);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            b[e] = fmaf(mu, b[e], g[e]);
-            y[e] = nesterov ? fmaf(mu, b[e], g[e]) : b[e];
+            b[pass][e] = fmaf(mu, b[pass][e], g[pass][e]);
+            y[e] = nesterov ? fmaf(mu, b[pass][e], g[pass][e]) : b[pass][e];
           }
-          store4(d.buf + o, vec, valid, b);
+          store4(d.buf + o[pass], vec[pass], valid[pass], b[pass]);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = g[e];
+          for (int e = 0; e < 4; ++e) y[e] = g[pass][e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (e >= valid) y[e] = 0.0f;
+          if (e >= valid[pass]) y[e] = 0.0f;
         if (!ns) {
-          float pv[4];
-          T* p = static_cast<T*>(d.p) + o;
-          load4(p, vec, valid, pv);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = fmaf(step_lr, y[e], pv[e] * decay);
-          store4(p, vec, valid, pv);
-          if (d.upd) store4(d.upd + o, vec, valid, y);
+          for (int e = 0; e < 4; ++e) pv[pass][e] = fmaf(step_lr, y[e], pv[pass][e] * decay);
+          store4(static_cast<T*>(d.p) + o[pass], vec[pass], valid[pass], pv[pass]);
+          if (d.upd) store4(d.upd + o[pass], vec[pass], valid[pass], y);
         }
       }
 #pragma unroll
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
       __syncthreads();
 #pragma unroll
       for (int pass = 0; pass < 4; ++pass) {
-        const int j = rl0 + 16 * pass;  // input column -> output row
+        const int j = rl0 + rstep * pass;  // input column -> output row
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = tile[cl + e][j];
@@ -217,15 +238,17 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
   using T = typename Elem<DT>::T;
   __shared__ float tile[kEwTile][kEwTile + 1];
   const int tid = threadIdx.x;
-  const int cl = (tid & 15) * 4;
-  const int rl0 = tid >> 4;
   for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
     const int mi = find_matrix(prefix, nmat, t);
     const MatDesc& d = descs[mi];
     if (!d.ns) continue;  // uniform per tile
+    const EwShape sh = ew_shape(d.tr != 0);
     const int local = t - d.ew_tile0;
     const int tr_ = local / d.ew_tiles_c;
-    const int r0 = tr_ * kEwTile, c0 = (local - tr_ * d.ew_tiles_c) * kEwTile;
+    const int r0 = tr_ * sh.rows, c0 = (local - tr_ * d.ew_tiles_c) * sh.cols;
+    const int cl = (tid % sh.tpr) * 4;
+    const int rl0 = tid / sh.tpr;
+    const int rstep = kEwThreads / sh.tpr;
     const int m = d.m, n = d.n, np = d.np;
     const float sc = scales[mi].c;
     const float step_lr = -lr * d.lr_scale;
@@ -233,7 +256,7 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
       // caller (r, c) is wide (c, r): stage the wide tile rows c0.., cols r0..
 #pragma unroll
       for (int pass = 0; pass < 4; ++pass) {
-        const int j = rl0 + 16 * pass;
+        const int j = rl0 + rstep * pass;
         float v[4];
         load4(d.xm + static_cast<long>(c0 + j) * np + r0 + cl, true, 4, v);
 #pragma unroll
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
     }
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
-      const int rl = rl0 + 16 * pass;
+      const int rl = rl0 + rstep * pass;
       const int r = r0 + rl, c = c0 + cl;
       if (r < m && c < n) {
         const int valid = min(4, n - c);
