@@ -37,8 +37,10 @@ struct alignas(16) MatDesc {
   float* buf;        // momentum buffer (muon step) or nullptr
   void* p;           // params (muon step) or x_out (ns only)
   float* upd;        // optional fp32 update output (original orientation)
-  float* xm;         // workspace: fp32 iterate X, Mp x Np, updated in place (bf16: its own
-                     // buffer; fp32: the same memory as xs0)
+  void* xm;          // workspace, Mp x Np.  fp32: the iterate X (the same memory as xs0).
+                     // bf16: the low half of the iterate, X - bf16(X) rounded to bf16, so
+                     // that X = hi + lo with hi the operand copy (16 significant bits);
+                     // updated in place.
   void* xs0;         // workspace: operand copy of X (dtype), Mp x Np, read on even steps
   void* xs1;         // workspace: operand copy of X, Mp x Np, read on odd steps (fp32: the
                      // iterate itself alternates between xs0 and xs1)

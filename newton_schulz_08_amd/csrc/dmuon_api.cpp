@@ -198,11 +198,12 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
   for (int k = 0; k < pl.n_ns; ++k) {
     MatPlan& mp = pl.mats[k];
     const size_t wide = static_cast<size_t>(mp.mp) * mp.np;
-    // bf16: fp32 iterate + two bf16 operand copies; fp32: the iterate itself
-    // alternates between two buffers (the update reads one, writes the other)
+    // bf16: the iterate is a bf16 pair, hi (two operand copies, one per step
+    // parity) + lo (in place); fp32: the iterate itself alternates between two
+    // buffers (the update reads one and writes the other)
     if (dt == kBF16) {
       mp.off_xm = off;
-      off = align_up(off + 4 * wide);
+      off = align_up(off + 2 * wide);
     }
     mp.off_xs0 = off;
     off = align_up(off + eb * wide);
@@ -341,7 +342,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     d.p = call.out[i];
     d.upd = call.upd ? call.upd[i] : nullptr;
     if (mp.ns) {
-      d.xm = reinterpret_cast<float*>(ws + mp.off_xm);
+      d.xm = ws + mp.off_xm;
       d.xs0 = ws + mp.off_xs0;
       d.xs1 = ws + mp.off_xs1;
       d.a = ws + mp.off_a;

@@ -8,8 +8,9 @@
 //     p <- p (1 - lr wd) - lr * s * Y, update_out <- Y  (blog VanillaMuon non-matrix
 //     branch, with the decoupled weight decay of the training guide's optimizer)
 //   Newton-Schulz matrices: Y is written, unnormalised, in the wide
-//   orientation as the fp32 iterate and (bf16) its operand copy; a tall
-//   matrix's tile goes through an LDS transpose so both sides stay coalesced.
+//   orientation as the iterate (fp32, or for bf16 the pair hi = bf16(Y),
+//   lo = bf16(Y - hi)); a tall matrix's tile goes through an LDS transpose so
+//   both sides stay coalesced.
 //   The 1/||Y|| scale is folded into the first Newton-Schulz step instead of a
 //   second pass.
 // norm_finalize_kernel -- fixed-order sum of each matrix's tile partials.
@@ -64,6 +65,37 @@ __device__ __forceinline__ void store4(T* __restrict__ dst, bool vec, int valid,
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (e < valid) gmem(dst)[e] = from_f32<T>(v[e]);
+  }
+}
+
+// Four consecutive elements of the wide iterate X at element offset w.  fp32:
+// X itself (xm, the same memory as xs0).  bf16: the pair hi = bf16(X) (the
+// operand copy xs0) and lo = bf16(X - hi) (xm).
+template <int DT>
+__device__ __forceinline__ void store_iterate(const MatDesc& d, long w, const float (&x)[4]) {
+  if constexpr (DT == kBF16) {
+    float hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = to_f32(from_f32<__bf16>(x[e]));
+      lo[e] = x[e] - hi[e];
+    }
+    store4(static_cast<__bf16*>(d.xs0) + w, true, 4, hi);
+    store4(static_cast<__bf16*>(d.xm) + w, true, 4, lo);
+  } else {
+    store4(static_cast<float*>(d.xm) + w, true, 4, x);
+  }
+}
+template <int DT>
+__device__ __forceinline__ void load_iterate(const MatDesc& d, long w, float (&x)[4]) {
+  if constexpr (DT == kBF16) {
+    float lo[4];
+    load4(static_cast<const __bf16*>(d.xs0) + w, true, 4, x);
+    load4(static_cast<const __bf16*>(d.xm) + w, true, 4, lo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] += lo[e];
+  } else {
+    load4(static_cast<const float*>(d.xm) + w, true, 4, x);
   }
 }
 
@@ -169,10 +201,8 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
       if (ns) {
         // the covered extent is padded to 256, so every tile position exists
         if (!trn) {
-          // wide: caller rows are rows of X (fp32 iterate; bf16 operand copy)
-          const long w = static_cast<long>(r) * np + c;
-          store4(d.xm + w, true, 4, y);
-          if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs0) + w, true, 4, y);
+          // wide: caller rows are rows of X
+          store_iterate<DT>(d, static_cast<long>(r) * np + c, y);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) tile[rl][cl + e] = y[e];
@@ -189,9 +219,7 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = tile[cl + e][j];
-        const long w = static_cast<long>(c0 + j) * np + r0 + cl;
-        store4(d.xm + w, true, 4, v);
-        if constexpr (DT == kBF16) store4(static_cast<T*>(d.xs0) + w, true, 4, v);
+        store_iterate<DT>(d, static_cast<long>(c0 + j) * np + r0 + cl, v);
       }
     }
 
@@ -258,7 +286,7 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
       for (int pass = 0; pass < 4; ++pass) {
         const int j = rl0 + rstep * pass;
         float v[4];
-        load4(d.xm + static_cast<long>(c0 + j) * np + r0 + cl, true, 4, v);
+        load_iterate<DT>(d, static_cast<long>(c0 + j) * np + r0 + cl, v);
 #pragma unroll
         for (int e = 0; e < 4; ++e) tile[j][cl + e] = v[e];
       }
@@ -276,7 +304,7 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
 #pragma unroll
           for (int e = 0; e < 4; ++e) u[e] = tile[cl + e][rl];
         } else {
-          load4(d.xm + static_cast<long>(r) * np + c, true, 4, u);
+          load_iterate<DT>(d, static_cast<long>(r) * np + c, u);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) u[e] *= sc;

@@ -145,6 +145,12 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                : "memory");
 }
 
+// The same with a full 64-bit source address per lane (no scalar base).
+__device__ __forceinline__ void lds_dma16_addr(const void* src, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_dst)
+               : "memory");
+}
+
 template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Wave grid of a 256x256 tile: 2 waves along M (128 rows each) and
@@ -594,19 +600,25 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   const float gamma = (step == 0) ? scales[tr.mat].c : 1.0f;
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
   const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
-  // fp32 iterate: bf16 keeps it in place in xm; for fp32 the operand copies
-  // are the iterate, so it moves from xq to xs_next
-  const float* xold = (DT == kBF16) ? d.xm : reinterpret_cast<const float*>(xq);
-  float* xnew = (DT == kBF16) ? d.xm : reinterpret_cast<float*>(xs_next);
+  // The iterate: fp32 moves from xq to xs_next; bf16 is the pair hi (xq, then
+  // xs_next) + lo (xm, in place)
+  const float* xold = reinterpret_cast<const float*>(xq);
+  float* xnew = reinterpret_cast<float*>(xs_next);
+  __bf16* xlo = static_cast<__bf16*>(d.xm);
   const bool trn = d.tr != 0;
   const float step_lr = -lr * d.lr_scale;
   // The tile is finished in four 64-row quarters through two 64 KB LDS
-  // buffers.  Quarter q's fp32 iterate rows arrive by LDS-DMA in the staging
-  // layout, the waves holding its accumulators replace them in place by
-  // gamma (1.5 X - 0.5 A X), and then every wave stores rows from LDS.
-  // Quarter q + 1's DMA is issued before quarter q's stores, so the wait for
-  // it (vmcnt counts loads and stores in issue order) leaves those stores in
-  // flight.
+  // buffers.  Quarter q is tile rows 32 q .. 32 q + 31 and 128 + 32 q ..
+  // 128 + 32 q + 31, i.e. accumulator block mi = q of every wave, so all
+  // eight waves share each quarter's work.  Its iterate rows arrive by
+  // LDS-DMA (fp32: 16-byte chunk c of a row holds columns 4c..4c+3; bf16:
+  // chunk 2c holds hi and chunk 2c + 1 lo of columns 8c..8c+7); each wave
+  // replaces its part by gamma (cx X + cax A X) in fp32 (for bf16 the two
+  // lanes sharing a chunk pair read it in the same instructions, then write
+  // their fp32 columns over it); then every wave reads its rows into
+  // registers, the buffer is handed to quarter q + 2's DMA, and the rows are
+  // stored.  vmcnt counts loads and stores in issue order, so each wait for a
+  // quarter's DMA leaves the stores issued after it in flight.
   constexpr int kQRows = 64;
   constexpr int kQBytes = kQRows * 1024;
   constexpr int kDmaRows = kQRows / (kThreads / 64);         // rows per wave per quarter
@@ -614,19 +626,29 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   constexpr int kColIt = 256 * (kQRows / 8) / kThreads;      // column segments per thread per quarter
   // store instructions per thread per quarter on a non-final step
   constexpr int kStoresQ = (DT == kBF16) ? 2 * kRowIt : kRowIt;
+  static_assert(2 * kStoresQ + kDmaRows < 64, "vmcnt range");
   const int c = tid & 63, col = Ct + 4 * c;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, lh = lane >> 5;
   const int cbase = (wave % Grid::kWN) * kBN * 8;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+  // tile row of row i (0..63) of quarter q's buffer
+  auto qrow = [](int q, int i) { return (i < 32) ? 32 * q + i : 96 + 32 * q + i; };
+  const char* xtile = uniform_ptr(reinterpret_cast<const char*>(xold + static_cast<long>(Rt) * np + Ct));
+  const char* hi_tile = xq + (static_cast<long>(Rt) * np + Ct) * 2;
+  const char* lo_tile = reinterpret_cast<const char*>(xlo + static_cast<long>(Rt) * np + Ct);
   auto dma_quarter = [&](int q) {
-    const char* xb = uniform_ptr(reinterpret_cast<const char*>(xold + static_cast<long>(Rt + kQRows * q) * np + Ct));
     const uint32_t dst = lds0 + (q & 1) * kQBytes;
 #pragma unroll
     for (int i = 0; i < kDmaRows; ++i) {
       const int r = wave * kDmaRows + i;
-      const uint32_t voff = static_cast<uint32_t>(r * np * 4 + 16 * (lane ^ ((r ^ (r >> 3)) & 63)));
-      lds_dma16(xb, voff, dst + r * 1024);
+      const int ls = lane ^ ((r ^ (r >> 3)) & 63);   // logical chunk of this lane's slot
+      if constexpr (DT == kBF16) {
+        const char* src = ((ls & 1) ? lo_tile : hi_tile) + static_cast<long>(qrow(q, r)) * np * 2 + (ls >> 1) * 16;
+        lds_dma16_addr(src, dst + r * 1024);
+      } else {
+        lds_dma16(xtile, static_cast<uint32_t>(qrow(q, r) * np * 4 + 16 * ls), dst + r * 1024);
+      }
     }
   };
   block_product<DT, kWaves, true>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
@@ -639,73 +661,98 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     char* buf = lds + (q & 1) * kQBytes;
-    if (wr == (q >> 1)) {
+    {
+      // all reads of the block first, then the updates (one LDS round trip)
+      float4 xv[kBN][4];
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        const int mi = 2 * (q & 1) + m2;
-        // all reads of the block row first, then the updates (one LDS round trip)
-        float4 xv[kBN][4];
+      for (int ni = 0; ni < kBN; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < kBN; ++ni)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            xv[ni][g] = *reinterpret_cast<const float4*>(buf + stage_off(32 * m2 + li, cbase + 8 * ni + 2 * g + lh));
-#pragma unroll
-        for (int ni = 0; ni < kBN; ++ni)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 x = xv[ni][g];
-            const f32x16& ax = acc[mi][ni];
-            *reinterpret_cast<float4*>(buf + stage_off(32 * m2 + li, cbase + 8 * ni + 2 * g + lh)) =
-                make_float4(gamma * (cx * x.x + cax * ax[4 * g]), gamma * (cx * x.y + cax * ax[4 * g + 1]),
-                            gamma * (cx * x.z + cax * ax[4 * g + 2]), gamma * (cx * x.w + cax * ax[4 * g + 3]));
+        for (int g = 0; g < 4; ++g) {
+          const int r = 32 * wr + li, c4 = cbase + 8 * ni + 2 * g + lh;
+          if constexpr (DT == kBF16) {
+            // columns 4 c4 .. 4 c4 + 3: half lh of chunk pair (c4 & ~1, c4 | 1)
+            const bf16x4 h = *reinterpret_cast<const bf16x4*>(buf + stage_off(r, c4 & ~1) + 8 * lh);
+            const bf16x4 l = *reinterpret_cast<const bf16x4*>(buf + stage_off(r, c4 | 1) + 8 * lh);
+            xv[ni][g] = make_float4(static_cast<float>(h[0]) + static_cast<float>(l[0]),
+                                    static_cast<float>(h[1]) + static_cast<float>(l[1]),
+                                    static_cast<float>(h[2]) + static_cast<float>(l[2]),
+                                    static_cast<float>(h[3]) + static_cast<float>(l[3]));
+          } else {
+            xv[ni][g] = *reinterpret_cast<const float4*>(buf + stage_off(r, c4));
           }
-      }
+        }
+#pragma unroll
+      for (int ni = 0; ni < kBN; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 x = xv[ni][g];
+          const f32x16& ax = acc[q][ni];
+          *reinterpret_cast<float4*>(buf + stage_off(32 * wr + li, cbase + 8 * ni + 2 * g + lh)) =
+              make_float4(gamma * (cx * x.x + cax * ax[4 * g]), gamma * (cx * x.y + cax * ax[4 * g + 1]),
+                          gamma * (cx * x.z + cax * ax[4 * g + 2]), gamma * (cx * x.w + cax * ax[4 * g + 3]));
+        }
     }
     __syncthreads();
     if (!last) {
-      // iterate rows: fp32 and (bf16) the next step's operand copy, in
-      // batches of four rows, LDS reads first, then the stores
-#pragma unroll
-      for (int kb = 0; kb < kRowIt; kb += 4) {
-        f32v4 rv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float4 v4 = stage_ld4(buf, (tid >> 6) + (kThreads / 64) * (kb + k), c);
-          rv[k] = f32v4{v4.x, v4.y, v4.z, v4.w};
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int row = Rt + kQRows * q + (tid >> 6) + (kThreads / 64) * (kb + k);
-          const float xn[4] = {rv[k].x, rv[k].y, rv[k].z, rv[k].w};
-          vst4(xnew + static_cast<long>(row) * np + col, xn);
-          if constexpr (DT == kBF16) vst4(xs_next + static_cast<long>(row) * np + col, xn);
-        }
-      }
-    } else if (!trn) {
-      // final step, wide matrix: caller rows
+      // iterate rows: fp32, or the bf16 pair (hi is the next step's operand copy)
+      f32v4 rv[kRowIt];
 #pragma unroll
       for (int k = 0; k < kRowIt; ++k) {
-        const int r = (tid >> 6) + (kThreads / 64) * k;
-        const float4 v4 = stage_ld4(buf, r, c);
-        const float xn[4] = {v4.x, v4.y, v4.z, v4.w};
-        write_caller<T, 4>(d, mode, step_lr, decay, Rt + kQRows * q + r, col, xn);
+        const float4 v4 = stage_ld4(buf, (tid >> 6) + (kThreads / 64) * k, c);
+        rv[k] = f32v4{v4.x, v4.y, v4.z, v4.w};
       }
-    } else {
-      // final step, tall matrix: wide (row, col) is caller (col, row)
+      if (q < 2) {
+        __syncthreads();         // every wave holds its rows: the buffer is free
+        dma_quarter(q + 2);
+      }
 #pragma unroll
-      for (int j = 0; j < kColIt; ++j) {
-        const int qq = tid + kThreads * j, sgi = qq & 7, col8 = qq >> 3;
-        float v[8];
-        stage_col8(buf, sgi, col8, v);
-        write_caller<T, 8>(d, mode, step_lr, decay, Ct + col8, Rt + kQRows * q + 8 * sgi, v);
+      for (int k = 0; k < kRowIt; ++k) {
+        const int row = Rt + qrow(q, (tid >> 6) + (kThreads / 64) * k);
+        const float xn[4] = {rv[k].x, rv[k].y, rv[k].z, rv[k].w};
+        if constexpr (DT == kBF16) {
+          float hi[4], lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = static_cast<float>(static_cast<__bf16>(xn[e]));
+            lo[e] = xn[e] - hi[e];
+          }
+          vst4(xs_next + static_cast<long>(row) * np + col, hi);
+          vst4(xlo + static_cast<long>(row) * np + col, lo);
+        } else {
+          vst4(xnew + static_cast<long>(row) * np + col, xn);
+        }
       }
-    }
-    if (q < 3) {
-      if (!last) wait_vmcnt<kStoresQ>();  // quarter q + 1 landed; q's stores stay in flight
-      else wait_vmcnt<0>();
-      __syncthreads();
-      if (q < 2) dma_quarter(q + 2);               // into the buffer quarter q just released
+      // wait for quarter q + 1's DMA; what was issued after it stays in flight
+      if (q == 0) wait_vmcnt<kDmaRows + kStoresQ>();
+      else if (q == 1) wait_vmcnt<2 * kStoresQ + kDmaRows>();
+      else if (q == 2) wait_vmcnt<2 * kStoresQ>();
+      if (q < 3) __syncthreads();
+    } else {
+      if (!trn) {
+        // final step, wide matrix: caller rows
+#pragma unroll
+        for (int k = 0; k < kRowIt; ++k) {
+          const int r = (tid >> 6) + (kThreads / 64) * k;
+          const float4 v4 = stage_ld4(buf, r, c);
+          const float xn[4] = {v4.x, v4.y, v4.z, v4.w};
+          write_caller<T, 4>(d, mode, step_lr, decay, Rt + qrow(q, r), col, xn);
+        }
+      } else {
+        // final step, tall matrix: wide (row, col) is caller (col, row); an
+        // 8-row segment never straddles the quarter's two 32-row blocks
+#pragma unroll
+        for (int j = 0; j < kColIt; ++j) {
+          const int qq = tid + kThreads * j, sgi = qq & 7, col8 = qq >> 3;
+          float v[8];
+          stage_col8(buf, sgi, col8, v);
+          write_caller<T, 8>(d, mode, step_lr, decay, Ct + col8, Rt + qrow(q, 8 * sgi), v);
+        }
+      }
+      if (q < 3) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (q < 2) dma_quarter(q + 2);  // into the buffer quarter q just released
+      }
     }
   }
 }

@@ -81,9 +81,10 @@ def test_workspace_layout_exact(lib):
     assert st == 0
     mb = 512 * 2048 * 4
     assert nbytes == 256 + 256 + 1024 + 256 + 2 * mb + 512 * 512 * 4
-    # bf16: fp32 iterate + two bf16 operand copies + bf16 Gram
+    # bf16: the iterate's low half + two operand copies (its high half, one per
+    # step parity) + bf16 Gram
     st, nb16 = _ws(lib, [(512, 2048)], dt=1)
-    assert nb16 == 256 + 256 + 1024 + 256 + 512 * 2048 * (4 + 2 + 2) + 512 * 512 * 2
+    assert nb16 == 256 + 256 + 1024 + 256 + 512 * 2048 * (2 + 2 + 2) + 512 * 512 * 2
     # a three-term polynomial adds the m' x m' buffer B = c1 A + c2 A^2
     st, nb3 = _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(terms=3, coeffs=(3.4445, -4.775, 2.0315)))
     assert st == 0 and nb3 == nb16 + 512 * 512 * 2
