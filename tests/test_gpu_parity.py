@@ -93,6 +93,17 @@ def check_against_oracle(cfg, res, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.0
     return worst
 
 
+# ------------------------------------------------------------------ maximum dimension
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_maximum_dimension(dtype):
+    """A wide and a tall matrix at DMUON_MAX_DIM (65536) on their long side, with
+    ragged short sides: the largest row pitches and operand offsets any call can
+    produce."""
+    cfg = _adhoc([(200, 65536), (65536, 300)], dtype, 71)
+    res = run_muon(cfg, ns_steps=3)
+    check_against_oracle(cfg, res, ns_steps=3)
+
+
 # ------------------------------------------------------------------ small / ragged
 RAGGED = [(600, 1100), (1100, 600), (300, 700), (257, 1000), (1000, 130), (250, 400), (3, 33333),
           (50, 70), (2048, 32), (512, 512)]
@@ -151,6 +162,42 @@ def test_zero_gradient_gives_zero_update():
         assert torch.equal(p, p0)
         assert torch.count_nonzero(u).item() == 0
         assert norms.item() == 0.0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rank_one_gradient(dtype):
+    """A rank-one gradient u v^T: its normalised singular value is 1, a fixed
+    point of every step of the cubic map, so U = u v^T / (|u| |v|)."""
+    rng = np.random.default_rng(72)
+    for rows, cols in ((384, 1000), (1000, 384)):
+        uvec, vvec = rng.standard_normal(rows), rng.standard_normal(cols)
+        g64 = np.outer(uvec, vvec)
+        g = torch.from_numpy(g64.astype(np.float32)).cuda().to(TORCH_DT[dtype])
+        gh = to_host_f64(g)                      # the exact input after rounding to dtype
+        out = nsa.ns_batched([g], ns_steps=5)[0]
+        want = oracle.newton_schulz(gh, 5)
+        closed = g64 / (np.linalg.norm(uvec) * np.linalg.norm(vvec))
+        got = to_host_f64(out)
+        assert rel_fro(got, want) <= TOL[dtype]
+        assert rel_fro(got, closed) <= TOL[dtype]
+
+
+def test_nonfinite_matrix_does_not_leak():
+    """A NaN in one matrix's gradient makes that matrix's update NaN (its norm is
+    NaN) and leaves every other matrix of the batch exactly as when it runs alone."""
+    cfg = _adhoc([(512, 768), (256, 1024)], "bf16", 73)
+    g = [to_device(gen.draw_matrix(cfg, i, gen.GRAD)) for i in range(2)]
+    p = [to_device(gen.draw_matrix(cfg, i, gen.WEIGHT)) for i in range(2)]
+    g[0][3, 5] = float("nan")
+    pa = [t.clone() for t in p]
+    u = [torch.zeros(t.shape, dtype=torch.float32, device="cuda") for t in p]
+    nsa.muon_step(pa, g, [torch.zeros(t.shape, device="cuda") for t in p], update_out=u)
+    pb = p[1].clone()
+    ub = torch.zeros(pb.shape, dtype=torch.float32, device="cuda")
+    nsa.muon_step([pb], [g[1]], [torch.zeros(pb.shape, device="cuda")], update_out=[ub])
+    torch.cuda.synchronize()
+    assert torch.isnan(u[0]).all()
+    assert torch.equal(u[1], ub) and torch.equal(pa[1], pb)
 
 
 def test_empty_batch_is_noop():
