@@ -170,19 +170,22 @@ struct WaveGrid {
 //   QN == false: like P, 256 rows (j) with K contiguous (the Gram: rows of X);
 //   QN == true:  K rows of 256 columns (j) with j contiguous (the update: X
 //                itself); Q0 points at row 0, column j0, pitch ldq_bytes.
-// kbytes is the contraction length in bytes (a multiple of 128, at least
-// 512).  after_last_barrier() runs once every wave has read its last operand
-// fragment: from then on the caller owns all of the LDS, while the final
-// MFMAs are still in flight.
+// kbytes is the contraction length in bytes (a multiple of 256 elements).
+// before_last_stage(i), i = 0 .. 2 * 256 / kWaves / 8 - 1, issues the
+// caller's own loads into the first 64 KB of LDS while the last stage is
+// multiplied (one per call, spread between MFMAs).  after_last_barrier() runs
+// once every wave has read its last operand fragment: from then on the caller
+// owns all of the LDS, while the final MFMAs are still in flight.
 //
 // Global -> LDS: global_load_lds_dwordx4 writes lane l's 16 bytes to
 // LDS[M0 + 16 l], so one wave instruction fills 1 KB of a stage.  Each lane
 // fetches the source chunk that belongs in its slot of the XOR-swizzled
 // layout the fragment reads expect, so there is no VGPR staging.
-template <int DT, int kWaves, bool QN, typename AfterLastBarrier>
+template <int DT, int kWaves, bool QN, typename BeforeLastStage, typename AfterLastBarrier>
 __device__ __forceinline__ void block_product(const char* __restrict__ P0, int ldp_bytes,
                                               const char* __restrict__ Q0, int ldq_bytes, int kbytes, char* lds,
                                               f32x16 (&acc)[4][WaveGrid<kWaves>::kBN],
+                                              BeforeLastStage&& before_last_stage,
                                               AfterLastBarrier&& after_last_barrier) {
   using G = WaveGrid<kWaves>;
   constexpr int kBN = G::kBN;
@@ -315,64 +318,67 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
     }
   };
   // One sub-step: the MFMAs of register slot rs, with the next sub-step's
-  // fragment reads (from (rstage, rsub) into slot rs ^ 1) and DMA loads
-  // d0 .. d0 + nd - 1 of stage dstage spread between them, each group pinned
-  // in place so no burst of LDS or memory issues stalls the MFMA stream.
-  auto substep = [&](int rs, int rstage, int rsub, int dstage, int dkb, int d0, int nd) {
+  // fragment reads (from (rstage, rsub) into slot rs ^ 1) and nd DMA loads
+  // (dma(0) .. dma(nd - 1)) spread between them, each group pinned in place so
+  // no burst of LDS or memory issues stalls the MFMA stream.
+  auto substep = [&](int rs, int rstage, int rsub, auto&& dma, int nd) {
 #pragma unroll
     for (int j = 0; j < kMfma; ++j) {
       mfma_one(rs, j);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = j * kReads / kMfma; i < (j + 1) * kReads / kMfma; ++i) read_one(rstage, rsub, rs ^ 1, i);
-      if (nd > 0) {
 #pragma unroll
-        for (int i = j * (kDma / 2) / kMfma; i < (j + 1) * (kDma / 2) / kMfma; ++i)
-          if (i < nd) dma_one(dstage, dkb, d0 + i);
-      }
+      for (int i = j * nd / kMfma; i < (j + 1) * nd / kMfma; ++i) dma(i);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto no_dma = [](int) {};
 
   // Pipeline: stage kt is multiplied from buffer kt & 1 while stage kt + 1
   // lands in the other buffer.  Stage kt + 2's loads go into buffer kt & 1
-  // once the barrier after sub-step 2 has retired every read of it: half in
-  // sub-step 3 of stage kt, half in sub-step 0 of stage kt + 1.
+  // once the barrier after sub-step 2 has retired every read of it, spread
+  // over sub-step 3 of stage kt; they have until the barrier after sub-step 2
+  // of stage kt + 1 to land.  The buffer stage nk - 2 frees receives the
+  // caller's early loads instead (before_last_stage(0 .. kDma - 1)).  nk is
+  // even and at least 4: every contraction extent is a multiple of 256.
   const int nk = kbytes / 128;
 #pragma unroll
   for (int i = 0; i < kDma; ++i) dma_one(0, 0, i);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kDma / 2; ++i) dma_one(1, min(1, nk - 1) * 128, i);
+  for (int i = 0; i < kDma; ++i) dma_one(1, 128, i);
 #pragma unroll
   for (int i = 0; i < kReads; ++i) read_one(0, 0, 0, i);
   __builtin_amdgcn_sched_barrier(0);
-  for (int kt = 0; kt < nk - 1; ++kt) {
+  for (int kt = 0; kt < nk - 2; ++kt) {
     const int c = kt & 1;
-    substep(0, c, 1, c ^ 1, min(kt + 1, nk - 1) * 128, kDma / 2, kDma / 2);
-    substep(1, c, 2, 0, 0, 0, 0);
-    substep(0, c, 3, 0, 0, 0, 0);
+    substep(0, c, 1, no_dma, 0);
+    substep(1, c, 2, no_dma, 0);
+    substep(0, c, 3, no_dma, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // past the end the final stage is re-loaded into the idle buffer (in
-    // bounds, never used) so the loop body stays one basic block
-    substep(1, c ^ 1, 0, c, min(kt + 2, nk - 1) * 128, 0, kDma / 2);
+    substep(1, c ^ 1, 0, [&](int i) { dma_one(c, (kt + 2) * 128, i); }, kDma);
   }
+  // stage nk - 2: buffer 0 is free after its barrier
+  substep(0, 0, 1, no_dma, 0);
+  substep(1, 0, 2, no_dma, 0);
+  substep(0, 0, 3, no_dma, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  substep(1, 1, 0, before_last_stage, kDma);
   // final stage: no more loads; after its barrier nothing reads the operand
   // buffers again, so the caller may start filling LDS while the last
   // sub-step's MFMAs run
-  {
-    const int c = (nk - 1) & 1;
-    substep(0, c, 1, 0, 0, 0, 0);
-    substep(1, c, 2, 0, 0, 0, 0);
-    substep(0, c, 3, 0, 0, 0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    after_last_barrier();
+  substep(0, 1, 1, no_dma, 0);
+  substep(1, 1, 2, no_dma, 0);
+  substep(0, 1, 3, no_dma, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  after_last_barrier();
 #pragma unroll
-    for (int j = 0; j < kMfma; ++j) mfma_one(1, j);
-  }
+  for (int j = 0; j < kMfma; ++j) mfma_one(1, j);
 }
 
 #ifndef DMUON_WAVES
@@ -522,7 +528,8 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
     for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
   block_product<DT, kWaves, false>(xs + static_cast<long>(tr.bi) * kTile * ld, ld,
-                                   xs + static_cast<long>(tr.bj) * kTile * ld, ld, kdim * EB, lds, acc, [] {});
+                                   xs + static_cast<long>(tr.bj) * kTile * ld, ld, kdim * EB, lds, acc,
+                                   [](int) {}, [] {});
 
   const float alpha = square ? cq : (step == 0 ? scales[tr.mat].c2 : 1.0f);
   T* a = static_cast<T*>(square ? d.b : d.a);
@@ -637,25 +644,28 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   const char* xtile = uniform_ptr(reinterpret_cast<const char*>(xold + static_cast<long>(Rt) * np + Ct));
   const char* hi_tile = xq + (static_cast<long>(Rt) * np + Ct) * 2;
   const char* lo_tile = reinterpret_cast<const char*>(xlo + static_cast<long>(Rt) * np + Ct);
-  auto dma_quarter = [&](int q) {
+  // row i (0 .. kDmaRows - 1) of this wave's share of quarter q's DMA
+  auto dma_quarter_row = [&](int q, int i) {
     const uint32_t dst = lds0 + (q & 1) * kQBytes;
-#pragma unroll
-    for (int i = 0; i < kDmaRows; ++i) {
-      const int r = wave * kDmaRows + i;
-      const int ls = lane ^ ((r ^ (r >> 3)) & 63);   // logical chunk of this lane's slot
-      if constexpr (DT == kBF16) {
-        const char* src = ((ls & 1) ? lo_tile : hi_tile) + static_cast<long>(qrow(q, r)) * np * 2 + (ls >> 1) * 16;
-        lds_dma16_addr(src, dst + r * 1024);
-      } else {
-        lds_dma16(xtile, static_cast<uint32_t>(qrow(q, r) * np * 4 + 16 * ls), dst + r * 1024);
-      }
+    const int r = wave * kDmaRows + i;
+    const int ls = lane ^ ((r ^ (r >> 3)) & 63);   // logical chunk of this lane's slot
+    if constexpr (DT == kBF16) {
+      const char* src = ((ls & 1) ? lo_tile : hi_tile) + static_cast<long>(qrow(q, r)) * np * 2 + (ls >> 1) * 16;
+      lds_dma16_addr(src, dst + r * 1024);
+    } else {
+      lds_dma16(xtile, static_cast<uint32_t>(qrow(q, r) * np * 4 + 16 * ls), dst + r * 1024);
     }
   };
+  auto dma_quarter = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < kDmaRows; ++i) dma_quarter_row(q, i);
+  };
+  // quarter 0 lands in the buffer the second-to-last stage frees, a stage
+  // before the product ends; quarter 1 starts at the last barrier
+  static_assert(kDmaRows == 2 * Grid::kLoadsPerOperand, "one early load per main-loop DMA slot");
   block_product<DT, kWaves, true>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
-                                  xq + static_cast<long>(tr.bj) * kTile * EB, np * EB, mp * EB, lds, acc, [&] {
-    dma_quarter(0);
-    dma_quarter(1);
-  });
+                                  xq + static_cast<long>(tr.bj) * kTile * EB, np * EB, mp * EB, lds, acc,
+                                  [&](int i) { dma_quarter_row(0, i); }, [&] { dma_quarter(1); });
   wait_vmcnt<kDmaRows>();
   __syncthreads();
 #pragma unroll
