@@ -37,6 +37,9 @@
  * - The workspace must hold at least the queried number of bytes and must not
  *   be used by anything else until the enqueued work completes.  Two calls may
  *   run concurrently only with distinct workspaces and disjoint outputs.
+ * - The calls cannot be recorded into a HIP graph: each uploads its
+ *   descriptors from host memory that lives only for the call.  A call on a
+ *   stream that is capturing returns DMUON_ERR_INVALID_ARG.
  * - Argument errors are detected before anything is enqueued; nothing is
  *   modified in that case.  A later DMUON_ERR_HIP means a launch failed and the
  *   outputs are unspecified.
@@ -129,7 +132,9 @@ int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols
  * ns_config: NULL (the cubic map, gram backend) or a host configuration, read
  *            during the call; the workspace must be sized for the same one.
  * Every matrix is orthogonalised, whatever its size.  bf16 inputs run the
- * contractions on bf16 operands with fp32 accumulation and an fp32 iterate.
+ * contractions on bf16 operands with fp32 accumulation; between steps the
+ * iterate is kept as a bf16 pair hi + lo (16 significant bits), and all
+ * epilogue arithmetic is fp32.
  */
 int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out,
                      const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,

@@ -4,10 +4,15 @@
 // min(rows, cols), n' cols = max(rows, cols); both padded up to multiples of
 // kTile so the contraction kernels run without bounds checks):
 //
-//   xm  float32  Mp x Np  row-major   iterate (fp32 master copy)
-//   xs  dtype    Mp x Np  row-major   operand of the Gram product (aliases xm for fp32)
-//   xt  dtype    Np x Mp  row-major   transposed iterate, operand of A*X (two, ping-pong)
-//   a   dtype    Mp x Mp  row-major   Gram matrix X X^T (symmetric)
+//   xs0, xs1  dtype  Mp x Np  row-major  operand copies of X, one per step
+//                                        parity: step k reads xs[k % 2] (Gram and
+//                                        update) and its update epilogue writes
+//                                        xs[(k + 1) % 2].  fp32: the iterate itself;
+//                                        bf16: hi = bf16(X).
+//   xm        bf16   Mp x Np  row-major  bf16 only: lo = bf16(X - hi), updated in
+//                                        place (fp32: the same memory as xs0)
+//   a         dtype  Mp x Mp  row-major  Gram matrix X X^T (symmetric)
+//   b         dtype  Mp x Mp  row-major  c2 A A + c1 A, three-term maps only
 //
 // Padding rows/cols hold zeros, which every stage preserves.
 #pragma once

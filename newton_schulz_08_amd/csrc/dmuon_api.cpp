@@ -229,7 +229,10 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
 std::mutex g_dev_mu;
 std::map<int, int> g_dev_status;  // device -> status
 
-int check_device() {
+// The device must be a gfx950, and the stream must not be capturing a graph:
+// every call uploads its descriptors with hipMemcpyAsync from host memory that
+// lives only for the call, which a replayed graph would read after it is gone.
+int check_device(void* hip_stream) {
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
     (void)hipGetLastError();
@@ -237,17 +240,30 @@ int check_device() {
   }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(DMUON_ERR_HIP, "hipGetDevice failed");
-  std::lock_guard<std::mutex> lk(g_dev_mu);
-  auto it = g_dev_status.find(dev);
-  if (it != g_dev_status.end()) {
-    if (it->second != DMUON_OK) return fail(it->second, "current device is not gfx950");
-    return DMUON_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto it = g_dev_status.find(dev);
+    if (it == g_dev_status.end()) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(DMUON_ERR_HIP, "hipGetDeviceProperties failed");
+      const int st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? DMUON_OK : DMUON_ERR_UNSUPPORTED_ARCH;
+      g_dev_status[dev] = st;
+      if (st != DMUON_OK) return fail(st, std::string("current device is ") + prop.gcnArchName + ", not gfx950");
+    } else if (it->second != DMUON_OK) {
+      return fail(it->second, "current device is not gfx950");
+    }
   }
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(DMUON_ERR_HIP, "hipGetDeviceProperties failed");
-  const int st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? DMUON_OK : DMUON_ERR_UNSUPPORTED_ARCH;
-  g_dev_status[dev] = st;
-  if (st != DMUON_OK) return fail(st, std::string("current device is ") + prop.gcnArchName + ", not gfx950");
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(static_cast<hipStream_t>(hip_stream), &cs);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DMUON_ERR_HIP, std::string("hipStreamIsCapturing: ") + hipGetErrorString(e));
+  }
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(DMUON_ERR_INVALID_ARG,
+                "the stream is capturing a graph; the descriptor upload reads host memory that does not outlive "
+                "the call, so these calls cannot be recorded");
   return DMUON_OK;
 }
 
@@ -689,7 +705,7 @@ int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out, con
   if ((st = check_distinct(outs)) != DMUON_OK) return st;
   const Plan pl = make_plan(count, rows, cols, dtype, false, ns.terms == 3);
   if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
-  if ((st = check_device()) != DMUON_OK) return st;
+  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
   Call call{};
   call.mode = kModeNsOnly;
   call.in = x_in;
@@ -736,7 +752,7 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
   if ((st = check_distinct(ptrs)) != DMUON_OK) return st;
   const Plan pl = make_plan(count, rows, cols, dtype, true, ns.terms == 3);
   if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
-  if ((st = check_device()) != DMUON_OK) return st;
+  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
   Call call{};
   call.mode = kModeMuon;
   call.in = grads;
@@ -795,7 +811,7 @@ int dmuon_clip_grad_norm(int count, void* const* grads, const int64_t* numel, in
     return fail(DMUON_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                                          std::to_string(cp.total));
   if (!aligned(workspace, kAlign)) return fail(DMUON_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if ((st = check_device()) != DMUON_OK) return st;
+  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   char* ws = static_cast<char*>(workspace);
@@ -884,7 +900,7 @@ int dmuon_adamw_step(int count, void* const* params, const void* const* grads, f
     return fail(DMUON_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                                          std::to_string(ap.total));
   if (!aligned(workspace, kAlign)) return fail(DMUON_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if ((st = check_device()) != DMUON_OK) return st;
+  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   char* ws = static_cast<char*>(workspace);
@@ -947,10 +963,12 @@ const char* dmuon_status_string(int status) {
 const char* dmuon_last_error(void) { return g_last_error.c_str(); }
 
 const char* dmuon_backend_info(void) {
-  return "dmuon gfx950 | prologue: fused momentum/Nesterov/Frobenius partials, 64x64 LDS-transpose tiles"
-         " | syrk: lower-triangle 256x256 tiles + transposed mirror, v_mfma_f32_32x32x16_bf16 / 32x32x2_f32"
-         " | ns_gemm: 256x256 tiles, fused c0 X + c1 A X epilogue (cubic 1.5/-0.5 by default; three-term maps"
-         " add a c2 A^2 + c1 A square launch), last step writes p = p (1 - lr wd) - lr s U"
+  return "dmuon gfx950 | prologue: fused momentum/Nesterov/Frobenius partials, 16x256 tiles (64x64 with an"
+         " LDS transpose for tall matrices) | syrk: lower-triangle 256x256 tiles + transposed mirror,"
+         " v_mfma_f32_32x32x16_bf16 / 32x32x2_f32 | ns_gemm: 256x256 tiles, X read row-major through"
+         " ds_read_b64_tr_b16, fused c0 X + c1 A X epilogue (cubic 1.5/-0.5 by default; three-term maps"
+         " add a c2 A^2 + c1 A square launch), bf16 iterate kept as a hi/lo pair, last step writes"
+         " p = p (1 - lr wd) - lr s U"
          " | ragged batch: shape-grouped segments, per-XCD balanced tile shares | built " __DATE__;
 }
 

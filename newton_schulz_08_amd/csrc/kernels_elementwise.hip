@@ -1,6 +1,7 @@
 // HBM-bound kernels of the Muon step on gfx950.
 //
-// prologue_kernel  -- one pass over every matrix, 64x64 tiles, 256 threads:
+// prologue_kernel  -- one pass over every matrix, 256 threads per tile (16 x 256
+//   tiles; 64 x 64 for tall Newton-Schulz matrices):
 //     buf <- mu * buf + g                       (blog post VanillaMuon: mul_ then add_)
 //     Y   <- g + mu * buf  or  buf              (training guide: nesterov ns_input)
 //     partial sum of Y^2 per tile               (Frobenius norm of the NS input)

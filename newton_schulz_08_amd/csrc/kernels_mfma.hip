@@ -17,10 +17,12 @@
 // in square mode forms B = c2 A A + c1 A (A symmetric, so A A = A A^T, again
 // on lower-triangle tiles), and ns_gemm_kernel then uses B with c1 = 1.
 //
-// Both are the same "NT" block product C[i,j] = sum_k P[i,k] Q[j,k] with both
-// operands K-contiguous: the Gram uses P = Q = X (rows of X), the update uses
-// P = A and Q = X^T (rows of the transposed iterate, which the previous
-// epilogue keeps up to date).  Each 512-thread workgroup computes a 256x256
+// Both are the block product C[i,j] = sum_k P[i,k] Q[k,j] with P K-contiguous.
+// The Gram takes Q = X^T, i.e. Q's columns are rows of X, also K-contiguous
+// (P = X).  The update takes P = A and Q = X read row-major: its stages land in
+// LDS as K rows of 256 columns, and transposing LDS reads
+// (ds_read_b64_tr_b16; fp32: single-word reads) hand each lane the
+// K-consecutive values the MFMA expects.  Each 512-thread workgroup computes a 256x256
 // tile; its eight waves form a 2 x 4 grid of 128x64 blocks, each 4x2 blocks of
 // v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32), two waves
 // per SIMD.  K advances 128 bytes per stage (64 bf16 / 32 fp32) through a
@@ -104,7 +106,7 @@ __device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lo
     r.bj = t - bi * (bi + 1) / 2;
   } else {
     // groups of kGroupRows tile rows, walked column by column, so the tiles
-    // resident at one time share few A row panels and X^T row panels
+    // resident at one time share few P row panels and Q column panels
     constexpr int kGroupRows = 4;
     const int gsz = kGroupRows * sg.tn;
     const int grp = t / gsz;
@@ -394,10 +396,11 @@ constexpr int kThreads = Grid::kThreadsPerBlock;
 // product: lane (li, lh), register 4 g + q of block (mi, ni) is
 //   C[32 mi + li][32 (wc kBN + ni) + 8 g + 4 lh + q]
 // (rows relative to the wave's 128-row half), i.e. four consecutive columns of
-// one row.  The epilogue stages one 128 x 256 fp32 half-tile at a time in the
-// 128 KB of LDS the operand stages no longer need, then writes every output
-// with 16-byte lanes: rows for row-major outputs, 8-row column segments for
-// transposed ones.
+// one row.  The Gram epilogue stages one 128 x 256 fp32 half-tile at a time
+// in the 128 KB of LDS the operand stages no longer need, then writes every
+// output with 16-byte lanes: rows for row-major outputs, 8-row column
+// segments for transposed ones.  The update epilogue uses the same layout for
+// its 64-row quarters, one 64 KB buffer each.
 //
 // Staging layout: 16-byte chunk c (0..63) of row r (0..127) lives at chunk
 // c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 63.  Conflict-free for the three
@@ -601,8 +604,6 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
-
-
 
   const float gamma = (step == 0) ? scales[tr.mat].c : 1.0f;
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;

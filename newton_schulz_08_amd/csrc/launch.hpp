@@ -40,8 +40,8 @@ hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int nti
 
 // X <- g (cx X + cax M X) with M = A (poly == 0) or B (poly == 1); g = c at
 // step 0, else 1.  The product reads the operand copy of step `step` and the
-// epilogue writes the next step's copy (and, for bf16, the fp32 iterate in
-// place).  On the last step the result U is written to the caller:
+// epilogue writes the next step's copy (and, for bf16, the low half of the
+// iterate in place).  On the last step the result U is written to the caller:
 // p <- p * decay + step_lr * U (mode muon) or out = U (ns only).
 hipError_t launch_ns_gemm(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
                           int step, int last, int mode, float lr, float decay, float cx, float cax, int poly,
