@@ -99,6 +99,109 @@ def recorded_traffic(kernel):
     return None
 
 
+def _smi_json(args, timeout=30):
+    """amd-smi ... --json as a dict, or None (a child process; never raises)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", *args, "--json"], capture_output=True, text=True, timeout=timeout)
+        d = json.loads(r.stdout)
+        if isinstance(d, dict):
+            d = d.get("gpu_data", [d])
+        return d[0] if isinstance(d, list) and d else None
+    except Exception:
+        return None
+
+
+def _mhz(v):
+    """'2400 MHz' / '2400MHz' / {'value': 2400, ...} -> 2400.0, else None."""
+    try:
+        if isinstance(v, dict):
+            return float(v["value"])
+        return float(str(v).replace("MHz", "").strip())
+    except (KeyError, TypeError, ValueError):
+        return None
+
+
+def gpu_static_info():
+    """Product name, CU count and the highest graphics clock level, read with
+    amd-smi before this process touches the GPU."""
+    d = _smi_json(["static", "--asic", "--clock"])
+    if not d:
+        return {}
+    asic, clk = d.get("asic", {}), d.get("clock", {})
+    levels = (clk.get("sys") or {}).get("frequency_levels") or {}
+    top = [m for m in (_mhz(v) for v in levels.values()) if m]
+    return {"market_name": asic.get("market_name"), "num_compute_units": asic.get("num_compute_units"),
+            "max_gfx_clock_mhz": max(top) if top else None}
+
+
+def clock_sampler(path, parent):
+    """Child-process loop: sample the graphics clocks (every XCD) and the power
+    with amd-smi into `path`, one JSON line each, until the parent exits (or
+    20 minutes pass)."""
+    t_end = time.time() + 1200
+    with open(path, "w") as f:
+        while os.getppid() == parent and time.time() < t_end:
+            t0 = time.time()
+            d = _smi_json(["metric", "--clock", "--power"], timeout=20)
+            rec = {"t0": t0, "t1": time.time()}
+            if d:
+                clk = d.get("clock") or {}
+                rec["gfx_mhz"] = [m for k, v in sorted(clk.items()) if k.startswith("gfx_") and isinstance(v, dict)
+                                  for m in [_mhz(v.get("clk"))] if m]
+                power = d.get("power") or {}
+                rec["power_w"] = {k: float(v["value"]) for k, v in power.items()
+                                  if isinstance(v, dict) and isinstance(v.get("value"), (int, float))}
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+            time.sleep(0.2)
+
+
+def start_clock_sampler():
+    """Start clock_sampler in a child process (before the GPU is touched).
+    Not under a profiler, which would follow the child."""
+    import subprocess
+    import tempfile
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return None
+    fd, path = tempfile.mkstemp(prefix="bench_clock_", suffix=".jsonl")
+    os.close(fd)
+    proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--clock-sampler", path, str(os.getpid())],
+                            stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    return proc, path
+
+
+def stop_clock_sampler(sampler, t0, t1):
+    """Stop the sampler; summarise the samples taken wholly inside [t0, t1]."""
+    if sampler is None:
+        return None
+    proc, path = sampler
+    proc.terminate()
+    try:
+        proc.wait(timeout=10)
+    except Exception:  # pragma: no cover
+        proc.kill()
+        proc.wait()
+    recs = []
+    try:
+        with open(path) as f:
+            recs = [json.loads(line) for line in f if line.strip()]
+    except (OSError, ValueError):
+        pass
+    os.unlink(path)
+    inside = [r for r in recs if r["t0"] >= t0 and r["t1"] <= t1 and r.get("gfx_mhz")]
+    if not inside:
+        return {"samples": 0}
+    mean = [sum(r["gfx_mhz"]) / len(r["gfx_mhz"]) for r in inside]
+    out = {"samples": len(inside), "gfx_clock_mhz_mean": sum(mean) / len(mean), "gfx_clock_mhz_min": min(mean),
+           "gfx_clock_mhz_max": max(mean)}
+    pw = [r.get("power_w", {}) for r in inside]
+    for k in sorted(set().union(*pw)):
+        vals = [p[k] for p in pw if k in p]
+        out[f"{k}_w_mean"] = sum(vals) / len(vals)
+    return out
+
+
 def metadata(torch):
     meta = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
             "peaks": {"bf16_mfma_tflops": PEAK_TFLOPS["bf16"], "f32_mfma_tflops": PEAK_TFLOPS["f32"],
@@ -109,10 +212,9 @@ def metadata(torch):
         meta["rocm"] = None
     try:
         prop = torch.cuda.get_device_properties(0)
-        meta["gpu"] = prop.name
+        meta["gpu"] = prop.name or None
         meta["gcn_arch"] = getattr(prop, "gcnArchName", None)
         meta["cus"] = prop.multi_processor_count
-        meta["max_clock_mhz"] = getattr(prop, "clock_rate", 0) / 1000.0 or None
     except Exception:  # pragma: no cover
         pass
     return meta
@@ -203,6 +305,9 @@ def reference_gemm(torch, n=8192, reps=30):
 
 
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--clock-sampler":
+        clock_sampler(sys.argv[2], int(sys.argv[3]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
@@ -222,6 +327,8 @@ def main():
                     help="skip timing the AdamW step over the non-matrix parameter set")
     ap.add_argument("--full-gram", action="store_true",
                     help="ablation: compute every Gram tile instead of the lower triangle plus its mirror")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="do not sample the GPU clock and power with amd-smi during the timed steps")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of GIB GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -233,6 +340,9 @@ def main():
 
     if args.full_gram:
         os.environ["DMUON_NS_KERNEL"] = "gemm"
+    # amd-smi runs in child processes started before this process touches the GPU
+    static_info = gpu_static_info() if args.copy_calibration <= 0 else {}
+    sampler = start_clock_sampler() if args.copy_calibration <= 0 and not args.no_clock_sample else None
     import torch
     import newton_schulz_08_amd as nsa
     from workloads import get_config
@@ -278,6 +388,7 @@ def main():
         nsa.profile_enable(True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    w0 = time.time()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record()
@@ -285,6 +396,8 @@ def main():
         ev[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    w1 = time.time()
+    clocks = stop_clock_sampler(sampler, w0, w1)
     nsa.profile_enable(False)
     kstats = nsa.profile_read() if args.profile else {}
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -317,6 +430,13 @@ def main():
                         "ns_gemm_kernel<bf16>" if cfg.dtype == "bf16" else "ns_gemm_kernel<f32>"),
                     "per_launch_flops": s["flops"] / max(s["launches"], 1),
                     "avg_launch_ms": s["total_ms"] / max(s["launches"], 1)}
+        top = static_info.get("max_gfx_clock_mhz")
+        if clocks and clocks.get("samples") and top:
+            # the published peak assumes the top clock; under this load the
+            # chip holds its power limit at a lower one
+            mhz = clocks["gfx_clock_mhz_mean"]
+            roofline["at_timed_clock"] = {"gfx_clock_mhz": mhz, "peak": peak * mhz / top,
+                                          "frac": achieved / (peak * mhz / top)}
     ns_kernel_ms = sum(kstats[k]["total_ms"] for k in ("syrk", "syrk_square", "ns_gemm") if k in kstats) / args.steps
 
     out = {
@@ -347,7 +467,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "backend": nsa.backend_info(),
-        "meta": metadata(torch),
+        "meta": {**metadata(torch), **static_info, "timed_region_clocks": clocks},
     }
     if not args.no_clip_bench:
         # after the timed steps: the clipping pass rescales the gradients in place
