@@ -98,12 +98,31 @@ __device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lo
   r.kdim = sg.kdim;
   r.full = sg.full;
   if (lower && !sg.full) {
-    // t -> (bi, bj), bj <= bi, row-major over the lower triangle
-    int bi = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-    while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
-    while (bi * (bi + 1) / 2 > t) --bi;
-    r.bi = bi;
-    r.bj = t - bi * (bi + 1) / 2;
+    // t -> (bi, bj), bj <= bi.  Groups of kTriGroupRows tile rows, each walked
+    // column by column, take the same index ranges as the rows do in
+    // row-major order: find t's row-major row, then place t in its group.
+    constexpr int kTriGroupRows = 4;
+    int row = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+    while ((row + 1) * (row + 2) / 2 <= t) ++row;
+    while (row * (row + 1) / 2 > t) --row;
+    const int r0 = row - row % kTriGroupRows;
+    const int h = min(sg.tm - r0, kTriGroupRows);
+    int tl = t - r0 * (r0 + 1) / 2;
+    if (tl < h * r0) {
+      // columns left of the group's own triangle: h tiles each
+      r.bi = r0 + tl % h;
+      r.bj = tl / h;
+    } else {
+      // the group's triangle, column bj holding rows bj .. r0 + h - 1
+      tl -= h * r0;
+      int bj = r0;
+      while (tl >= r0 + h - bj) {
+        tl -= r0 + h - bj;
+        ++bj;
+      }
+      r.bi = bj + tl;
+      r.bj = bj;
+    }
   } else {
     // groups of kGroupRows tile rows, walked column by column, so the tiles
     // resident at one time share few P row panels and Q column panels
