@@ -75,8 +75,14 @@ struct alignas(16) Segment {
   int tm, tn;         // tile grid: rows, cols of 256-tiles (SYRK: tm == tn)
   int kdim;           // contraction length in elements
   int full;           // Gram only: 1 = every tile, no mirror (measurement ablation); 0 = lower triangle
+  int ksplit;         // Gram only: > 1 = K cut into ksplit slices, summed by a second launch
+  int pad_;
+  float* part;        // ksplit > 1: kPartialFloats floats per (tile, slice), tile-major
 };
-static_assert(sizeof(Segment) == 32, "Segment layout");
+static_assert(sizeof(Segment) == 48, "Segment layout");
+
+// One fp32 256 x 256 partial product of a K slice.
+constexpr int kPartialFloats = 256 * 256;
 
 // Per-matrix scalars produced by the norm reduction.
 struct alignas(16) MatScale {

@@ -102,7 +102,25 @@ int resolve_ns_config(const dmuon_ns_config* cfg, int ns_steps, bool need_coeffs
 struct Group {
   int64_t mp, np;
   int first, count;   // range in the NS part of the descriptor order
+  int ks_gram = 1;    // K slices of the Gram product (and of the square product of a three-term map)
+  int ks_square = 1;
+  size_t off_part = 0;  // fp32 partial products of split Gram tiles
 };
+
+// K slices for the Gram product of a small matrix.  A matrix of at most two
+// 256-tile rows has at most 3 lower-triangle tiles, so a launch over a few of
+// them occupies a few CUs for the whole of K; cutting K into up to 8 slices
+// (each a multiple of 256) spreads it out, and a second launch sums the
+// slices in a fixed order.  The count depends only on the shape, so a
+// matrix's result never depends on the rest of the batch.
+int gram_ksplit(int64_t tile_rows, int64_t k) {
+  if (tile_rows > 2) return 1;
+  const int64_t units = k / kTile;
+  int best = 1;
+  for (int d = 2; d <= 8; ++d)
+    if (units % d == 0) best = d;
+  return best;
+}
 
 struct Plan {
   int dt = kF32;
@@ -170,8 +188,13 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
     return std::make_tuple(a.mp, a.np) < std::make_tuple(b.mp, b.np);
   });
   for (size_t k = 0; k < ns_mats.size(); ++k) {
-    if (pl.groups.empty() || pl.groups.back().mp != ns_mats[k].mp || pl.groups.back().np != ns_mats[k].np)
-      pl.groups.push_back(Group{ns_mats[k].mp, ns_mats[k].np, static_cast<int>(k), 0});
+    if (pl.groups.empty() || pl.groups.back().mp != ns_mats[k].mp || pl.groups.back().np != ns_mats[k].np) {
+      Group g{};
+      g.mp = ns_mats[k].mp;
+      g.np = ns_mats[k].np;
+      g.first = static_cast<int>(k);
+      pl.groups.push_back(g);
+    }
     pl.groups.back().count++;
   }
   pl.n_ns = static_cast<int>(ns_mats.size());
@@ -220,6 +243,19 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
     const double mm = static_cast<double>(std::min(mp.m, mp.n)), nn = static_cast<double>(std::max(mp.m, mp.n));
     pl.syrk_flops += mm * (mm + 1.0) * nn;
     pl.gemm_flops += 2.0 * mm * mm * nn + 3.0 * mm * nn;
+  }
+  // partial products of split Gram tiles, per shape group, sized for every
+  // tile of the grid (the direct backend computes all of them); the Gram and
+  // the square product run one after the other and share the region
+  for (Group& g : pl.groups) {
+    const int64_t T = g.mp / kTile;
+    g.ks_gram = gram_ksplit(T, g.np);
+    g.ks_square = three_terms ? gram_ksplit(T, g.mp) : 1;
+    const int ks = std::max(g.ks_gram, g.ks_square);
+    if (ks > 1) {
+      g.off_part = off;
+      off = align_up(off + sizeof(float) * kPartialFloats * static_cast<size_t>(T * T) * g.count * ks);
+    }
   }
   pl.total = std::max<size_t>(off, kAlign);
   return pl;
@@ -459,9 +495,13 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     s.tn = T;
     s.kdim = static_cast<int>(g.np);
     s.full = full_gram ? 1 : 0;
+    s.ksplit = g.ks_gram;
+    s.part = g.ks_gram > 1 ? reinterpret_cast<float*>(ws + g.off_part) : nullptr;
     syrk_segs.push_back(SegSpec{s, sf});
     Segment sq = s;
     sq.kdim = static_cast<int>(g.mp);
+    sq.ksplit = g.ks_square;
+    sq.part = g.ks_square > 1 ? reinterpret_cast<float*>(ws + g.off_part) : nullptr;
     square_segs.push_back(SegSpec{sq, qf});
     Segment q{};
     q.mat0 = g.first;
@@ -477,35 +517,51 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
   std::stable_sort(square_segs.begin(), square_segs.end(), by_k);
   std::stable_sort(gemm_segs.begin(), gemm_segs.end(), by_k);
 
-  auto batches = [](const std::vector<SegSpec>& segs) {
+  // Launch tables of at most kMaxSegPerLaunch segments.  A split Gram segment
+  // has one block per (tile, K slice) in the product launch; reduce tables
+  // hold only the split segments, one block per tile.
+  auto batches = [](const std::vector<SegSpec>& segs, bool reduce) {
     std::vector<std::pair<SegTable, std::pair<int, double>>> out;
-    for (size_t s0 = 0; s0 < segs.size(); s0 += kMaxSegPerLaunch) {
+    std::vector<SegSpec> use;
+    for (const SegSpec& sp : segs) {
+      if (!reduce || sp.s.ksplit > 1) use.push_back(sp);
+      if (!reduce && sp.s.ksplit > 1) use.back().s.ntiles *= sp.s.ksplit;
+    }
+    for (size_t s0 = 0; s0 < use.size(); s0 += kMaxSegPerLaunch) {
       SegTable st{};
       int tiles = 0;
       double fl = 0.0;
-      for (size_t k = s0; k < std::min(segs.size(), s0 + kMaxSegPerLaunch); ++k) {
-        Segment s = segs[k].s;
+      for (size_t k = s0; k < std::min(use.size(), s0 + kMaxSegPerLaunch); ++k) {
+        Segment s = use[k].s;
         s.tile0 = tiles;
         tiles += s.ntiles;
-        fl += segs[k].flops;
+        fl += use[k].flops;
         st.seg[st.nseg++] = s;
       }
       out.push_back({st, {tiles, fl}});
     }
     return out;
   };
-  const auto syrk_launches = batches(syrk_segs);
-  const auto square_launches = batches(square_segs);
-  const auto gemm_launches = batches(gemm_segs);
+  const auto syrk_launches = batches(syrk_segs, false);
+  const auto syrk_reduces = batches(syrk_segs, true);
+  const auto square_launches = batches(square_segs, false);
+  const auto square_reduces = batches(square_segs, true);
+  const auto gemm_launches = batches(gemm_segs, false);
   const bool three = call.ns.terms == 3;
 
   for (int step = 0; step < call.ns_steps; ++step) {
     const std::array<float, 3>& c = call.ns.coeffs[step];
     for (const auto& L : syrk_launches) {
       e = timed(kKSyrk, L.second.second, 0.0, stream, [&] {
-        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 0, 0.0f, 0.0f, stream);
+        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 0, 0.0f, 0.0f, 0, stream);
       });
       if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk launch: ") + hipGetErrorString(e));
+    }
+    for (const auto& L : syrk_reduces) {
+      e = timed(kKSyrk, 0.0, 0.0, stream, [&] {
+        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 0, 0.0f, 0.0f, 1, stream);
+      });
+      if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk sum launch: ") + hipGetErrorString(e));
     }
     // a step whose c2 is zero (a two-term set inside a three-term schedule)
     // needs no square product
@@ -514,9 +570,15 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
       // B = c2 A A + c1 A
       for (const auto& L : square_launches) {
         e = timed(kKSquare, L.second.second, 0.0, stream, [&] {
-          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 1, c[2], c[1], stream);
+          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 1, c[2], c[1], 0, stream);
         });
         if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk square launch: ") + hipGetErrorString(e));
+      }
+      for (const auto& L : square_reduces) {
+        e = timed(kKSquare, 0.0, 0.0, stream, [&] {
+          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 1, c[2], c[1], 1, stream);
+        });
+        if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk square sum launch: ") + hipGetErrorString(e));
       }
     }
     const int last = (step + 1 == call.ns_steps) ? 1 : 0;

@@ -80,19 +80,32 @@ __device__ __forceinline__ int xcd_share(int local, int n, int t0) {
 }
 
 struct TileRef {
-  int mat;   // NS descriptor index
-  int bi;    // tile row
-  int bj;    // tile col
+  int mat;     // NS descriptor index
+  int bi;      // tile row
+  int bj;      // tile col
   int kdim;
-  int full;  // Gram segment computing every tile (no mirror)
+  int full;    // Gram segment computing every tile (no mirror)
+  int ksplit;  // K slices of a split Gram segment (1: whole K in one block)
+  int slice;   // this block's K slice (product launch of a split segment)
+  float* part; // the tile's first partial product (split segments)
 };
 
-__device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lower) {
+// reduce: the block is one tile of a split segment's summing launch (one
+// block per tile); otherwise a split segment has one block per (tile, slice),
+// the slices of a tile adjacent.
+__device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lower, bool reduce = false) {
   int si = 0;
   while (si + 1 < st.nseg && st.seg[si + 1].tile0 <= block) ++si;
   const Segment& sg = st.seg[si];
-  const int local = xcd_share(block - sg.tile0, sg.ntiles, sg.tile0);
+  int local = xcd_share(block - sg.tile0, sg.ntiles, sg.tile0);
   TileRef r;
+  r.ksplit = sg.ksplit > 1 ? sg.ksplit : 1;
+  r.slice = 0;
+  if (r.ksplit > 1 && !reduce) {
+    r.slice = local % r.ksplit;
+    local /= r.ksplit;
+  }
+  r.part = r.ksplit > 1 ? sg.part + static_cast<long>(local) * r.ksplit * kPartialFloats : nullptr;
   r.mat = sg.mat0 + local / sg.tiles_per_mat;
   const int t = local % sg.tiles_per_mat;
   r.kdim = sg.kdim;
@@ -526,15 +539,47 @@ __device__ __forceinline__ void write_caller(const MatDesc& d, int mode, float s
   }
 }
 
+// A split Gram tile's partial product: thread tid's accumulator registers as
+// float4 j = 4 (mi kBN + ni) + g at float4 index j * kThreads + tid, so each
+// wave instruction moves 1 KB of consecutive memory and the summing launch
+// reads back exactly the registers this thread held.
+__device__ __forceinline__ void store_partial(float* part, const f32x16 (&acc)[4][kBN]) {
+  f32v4* dst = reinterpret_cast<f32v4*>(part) + threadIdx.x;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kBN; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc[mi][ni];
+        *gmem(dst + ((mi * kBN + ni) * 4 + g) * kThreads) =
+            f32v4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+      }
+}
+
+__device__ __forceinline__ void add_partial(const float* part, f32x16 (&acc)[4][kBN]) {
+  const f32v4* src = reinterpret_cast<const f32v4*>(part) + threadIdx.x;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kBN; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32v4 v = *gmem(src + ((mi * kBN + ni) * 4 + g) * kThreads);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mi][ni][4 * g + e] += v[e];
+      }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __restrict__ descs, SegTable st,
                                                           const MatScale* __restrict__ scales, int step,
-                                                          int square, float cq, float cl) {
+                                                          int square, float cq, float cl, int reduce) {
   using T = typename Elem<DT>::T;
   constexpr int EB = Elem<DT>::kBytes;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
 
-  const TileRef tr = locate(st, blockIdx.x, true);
+  const TileRef tr = locate(st, blockIdx.x, true, reduce != 0);
   const MatDesc& d = descs[tr.mat];
   const int mp = d.mp, np = d.np;
   // Gram of the iterate (K = Np), or the square of the symmetric Gram matrix
@@ -549,9 +594,21 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
 #pragma unroll
     for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
 
-  block_product<DT, kWaves, false>(xs + static_cast<long>(tr.bi) * kTile * ld, ld,
-                                   xs + static_cast<long>(tr.bj) * kTile * ld, ld, kdim * EB, lds, acc,
-                                   [](int) {}, [] {});
+  if (!reduce) {
+    // K slice of this block: all of K, or 1 / ksplit of it (a multiple of 256)
+    const int klen = kdim / tr.ksplit;
+    const long koff = static_cast<long>(tr.slice) * klen * EB;
+    block_product<DT, kWaves, false>(xs + static_cast<long>(tr.bi) * kTile * ld + koff, ld,
+                                     xs + static_cast<long>(tr.bj) * kTile * ld + koff, ld, klen * EB, lds, acc,
+                                     [](int) {}, [] {});
+    if (tr.ksplit > 1) {
+      store_partial(tr.part + static_cast<long>(tr.slice) * kPartialFloats, acc);
+      return;
+    }
+  } else {
+    // the tile's slices, summed in slice order
+    for (int s = 0; s < tr.ksplit; ++s) add_partial(tr.part + static_cast<long>(s) * kPartialFloats, acc);
+  }
 
   const float alpha = square ? cq : (step == 0 ? scales[tr.mat].c2 : 1.0f);
   T* a = static_cast<T*>(square ? d.b : d.a);
@@ -790,14 +847,14 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
 }  // namespace
 
 hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                       int step, int square, float cq, float cl, hipStream_t stream) {
+                       int step, int square, float cq, float cl, int reduce, hipStream_t stream) {
   if (ntiles <= 0) return hipSuccess;
   if (dt == kBF16)
     hipLaunchKernelGGL(syrk_kernel<kBF16>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, step,
-                       square, cq, cl);
+                       square, cq, cl, reduce);
   else
     hipLaunchKernelGGL(syrk_kernel<kF32>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, step,
-                       square, cq, cl);
+                       square, cq, cl, reduce);
   return hipGetLastError();
 }
 

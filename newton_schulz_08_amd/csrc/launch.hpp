@@ -35,8 +35,11 @@ hipError_t launch_apply_x0(int dt, const MatDesc* descs, const int* tile_prefix,
 //   square == 0: A = alpha X X^T (alpha = c^2 at step 0, else 1), X read from
 //                the operand copy of that step (xs0 on even steps, xs1 on odd).
 //   square == 1: B = cq A A + cl A (A symmetric, so A A = A A^T).
+// Segments with ksplit > 1 only write one fp32 partial product per (tile,
+// K slice); a second launch with reduce == 1 over a table of just those
+// segments (one block per tile) sums the slices in order and stores.
 hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
-                       int step, int square, float cq, float cl, hipStream_t stream);
+                       int step, int square, float cq, float cl, int reduce, hipStream_t stream);
 
 // X <- g (cx X + cax M X) with M = A (poly == 0) or B (poly == 1); g = c at
 // step 0, else 1.  The product reads the operand copy of step `step` and the

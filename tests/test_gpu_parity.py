@@ -315,6 +315,32 @@ def test_full_gram_ablation_matches(dtype, monkeypatch):
         assert rel_fro(to_host_f64(f), oracle.newton_schulz(x.as_f64(), 5)) <= TOL[dtype], s
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_gram_runs_in_k_slices(dtype):
+    """A matrix of at most two 256-tile rows has its Gram product cut into K
+    slices and summed by a second launch (2 Gram launches per step); three
+    tile rows or more take one.  Split and unsplit shapes in one batch, the
+    square product of a three-term map, and the direct backend all meet the
+    oracle."""
+    shapes = [(300, 2100), (2100, 300), (256, 1024), (800, 1500)]
+    cfg = _adhoc(shapes, dtype, 190 + (dtype == "bf16"))
+    xs = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(len(shapes))]
+    steps = 4
+    for split, launches in (([0, 1, 2], 2 * steps), ([3], steps)):
+        nsa.profile_read()
+        nsa.profile_enable(True)
+        nsa.ns_batched([to_device(xs[i]) for i in split], ns_steps=steps)
+        torch.cuda.synchronize()
+        nsa.profile_enable(False)
+        assert nsa.profile_read()["syrk"]["launches"] == launches, split
+    for kw in ({}, {"ns_backend": "direct"}, {"ns_coeffs": QUINTIC_CLASSICAL}):
+        outs = nsa.ns_batched([to_device(x) for x in xs], ns_steps=steps, **kw)
+        torch.cuda.synchronize()
+        for x, o, sh in zip(xs, outs, shapes):
+            want = oracle.newton_schulz(x.as_f64(), steps, coeffs=kw.get("ns_coeffs"))
+            assert rel_fro(to_host_f64(o), want) <= TOL[dtype], (kw, sh)
+
+
 QUINTIC_FAST = (3.4445, -4.7750, 2.0315)
 QUINTIC_CLASSICAL = (1.875, -1.25, 0.375)
 
