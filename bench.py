@@ -78,7 +78,33 @@ def cpu_baseline(cfg, sample_idx, ns_steps, mu, lr):
     desc = ", ".join(f"{cfg.matrices[i].name} {cfg.matrices[i].rows}x{cfg.matrices[i].cols}" for i in sample_idx)
     return {"value": (s + g) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one Muon step (k={ns_steps}) of {len(sample_idx)} matrices: {desc}; {dt:.2f} s wall, "
-                      f"float64 NumPy oracle"}
+                      f"float64 NumPy oracle",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def dense_equivalent_flops(shapes, ns_steps):
+    """What the same steps cost as two plain GEMMs each (4 m'^2 n' per matrix
+    and step: the full X X^T and A X), the count the method avoids with the
+    triangle; reported beside the algorithmic figure, never as % of peak."""
+    total = 0.0
+    for r, c in shapes:
+        if r * c < 100_000:
+            continue
+        m, n = float(min(r, c)), float(max(r, c))
+        total += 4.0 * m * m * n
+    return total * ns_steps
 
 
 def recorded_traffic(kernel):
@@ -463,6 +489,7 @@ def main():
                    "ns_coeffs": args.ns_coeffs if coeffs is None else f"{args.ns_coeffs} {coeffs}",
                    "weight_decay": args.weight_decay, "lr_scale": "moonlight" if args.moonlight else "one"},
         "ns_tflops_kernels": (ns_total / (ns_kernel_ms * 1e-3) / 1e12) if ns_kernel_ms > 0 else None,
+        "ns_tflops_dense_equivalent": dense_equivalent_flops(shapes, ns_steps) / (ms_per_step * 1e-3) / 1e12,
         "pct_mfma_peak": 100.0 * value / peak,
         "roofline": roofline,
         "kernels": kernels,

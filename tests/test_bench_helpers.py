@@ -22,6 +22,18 @@ def test_ns_flops_counts_the_method_work():
     assert s3 == syrk + 300 * 301 * 300 + 2 * 300 * 300 and g3 == gemm
 
 
+def test_dense_equivalent_counts_two_full_products():
+    assert bench.dense_equivalent_flops([(300, 1000), (100, 999)], ns_steps=2) == 2 * 4 * 300 * 300 * 1000
+    # about 4/3 of the method's own count for a wide matrix
+    syrk, gemm = bench.ns_flops([(4096, 14336)], 1)
+    assert 1.3 < bench.dense_equivalent_flops([(4096, 14336)], 1) / (syrk + gemm) < 1.34
+
+
+def test_cpu_model_is_a_string_or_none():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
+
+
 def test_recorded_traffic_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
     src = tmp_path / "newton_schulz_08_amd" / "csrc"
     src.mkdir(parents=True)
