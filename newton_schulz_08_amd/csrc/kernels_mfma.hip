@@ -62,10 +62,9 @@ template <typename T> __device__ __forceinline__ T from_f32(float v) { return st
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8).  Within a segment of n tiles whose blocks start at t0, give each XCD
-// one contiguous n/8 share of the segment's tile order, so every XCD gets the
-// same mix of long and short tiles and neighbouring tiles (which share
-// operand panels) meet in the same L2.  Returns the tile index for block
-// t0 + local; a bijection on [0, n).
+// one contiguous n/8 share of the segment's tile order, so neighbouring tiles
+// (which share operand panels) meet in the same L2.  Returns the tile index
+// for block t0 + local; a bijection on [0, n).
 __device__ __forceinline__ int xcd_share(int local, int n, int t0) {
   const int x = (t0 + local) & 7;
   int off = 0, first_x = 0;
@@ -77,6 +76,21 @@ __device__ __forceinline__ int xcd_share(int local, int n, int t0) {
     if (y == x) first_x = f;
   }
   return off + ((local - first_x) >> 3);
+}
+
+// Tile index for block t0 + local of a segment of n tiles, by rounds of 256:
+// in round c, the XCD that runs local indices = f (mod 8) takes the 32
+// consecutive tiles 256 c + 32 f .. 256 c + 32 f + 31 of the segment's tile
+// order, one per CU of the XCD.  Within an XCD the resident tiles are a
+// compact block of neighbours (shared operand panels in its L2), and at any
+// moment all eight XCDs work in the same 256-tile window, i.e. on the same
+// one or two matrices, whose panels the memory-side cache that every XCD
+// reads through can then hold.  Tiles after the last whole round are split
+// as in xcd_share.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_tile(int local, int n, int t0) {
+  const int base = (n >> 8) << 8;
+  if (local < base) return (((local >> 8) << 3) + (local & 7)) * 32 + ((local >> 3) & 31);
+  return base + xcd_share(local - base, n - base, t0);
 }
 
 struct TileRef {
@@ -97,7 +111,7 @@ __device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lo
   int si = 0;
   while (si + 1 < st.nseg && st.seg[si + 1].tile0 <= block) ++si;
   const Segment& sg = st.seg[si];
-  int local = xcd_share(block - sg.tile0, sg.ntiles, sg.tile0);
+  int local = xcd_tile(block - sg.tile0, sg.ntiles, sg.tile0);
   TileRef r;
   r.ksplit = sg.ksplit > 1 ? sg.ksplit : 1;
   r.slice = 0;
@@ -179,9 +193,10 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                : "memory");
 }
 
-// The same with a full 64-bit source address per lane (no scalar base).
-__device__ __forceinline__ void lds_dma16_addr(const void* src, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_dst)
+// The same with a full 64-bit source address per lane (no scalar base), as a
+// streaming (non-temporal) access: used for data read once per launch.
+__device__ __forceinline__ void lds_dma16_addr_nt(const void* src, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds_dst)
                : "memory");
 }
 
@@ -480,6 +495,17 @@ __device__ __forceinline__ void vst4(__bf16* p, const float* v) {
   for (int e = 0; e < 4; ++e) x[e] = static_cast<__bf16>(v[e]);
   *reinterpret_cast<gptr<bf16x4>>(gmem(p)) = x;
 }
+// Streaming (non-temporal) form, for the iterate an update epilogue writes: a
+// whole batch's iterate is far larger than any cache, so nothing of it
+// survives until the next launch reads it, and streaming it leaves the cached
+// operand panels that concurrent tiles share in place.
+__device__ __forceinline__ void vst4_nt(__bf16* p, const float* v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = static_cast<__bf16>(v[e]);
+  __builtin_nontemporal_store(x, reinterpret_cast<gptr<bf16x4>>(gmem(p)));
+}
 __device__ __forceinline__ void vld4(const float* p, float* v) {
   const f32v4 x = *reinterpret_cast<gptr<const f32v4>>(gmem(p));
   v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
@@ -728,7 +754,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
     const int ls = lane ^ ((r ^ (r >> 3)) & 63);   // logical chunk of this lane's slot
     if constexpr (DT == kBF16) {
       const char* src = ((ls & 1) ? lo_tile : hi_tile) + static_cast<long>(qrow(q, r)) * np * 2 + (ls >> 1) * 16;
-      lds_dma16_addr(src, dst + r * 1024);
+      lds_dma16_addr_nt(src, dst + r * 1024);
     } else {
       lds_dma16(xtile, static_cast<uint32_t>(qrow(q, r) * np * 4 + 16 * ls), dst + r * 1024);
     }
@@ -803,8 +829,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
             hi[e] = static_cast<float>(static_cast<__bf16>(xn[e]));
             lo[e] = xn[e] - hi[e];
           }
-          vst4(xs_next + static_cast<long>(row) * np + col, hi);
-          vst4(xlo + static_cast<long>(row) * np + col, lo);
+          vst4_nt(xs_next + static_cast<long>(row) * np + col, hi);
+          vst4_nt(xlo + static_cast<long>(row) * np + col, lo);
         } else {
           vst4(xnew + static_cast<long>(row) * np + col, xn);
         }
