@@ -135,3 +135,38 @@ def test_spectrum_flat_recurrence_on_gpu():
             for _ in range(k):
                 s = 1.5 * s - 0.5 * s ** 3
             assert np.max(np.abs(sv - s)) < 1e-5, (r, n, k, sv.min(), sv.max(), s)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["llama3_8b", "hybrid"])
+def test_every_matrix_independent_of_batch_order(key):
+    """Every matrix of a full-size set, through every tile of the batched
+    launches: the step must give bitwise the same update and parameters when
+    the batch is passed in reverse order, which moves each matrix's tiles to
+    other workgroups, XCDs and tile-order rounds (every shape group of these
+    sets has an even count, so no matrix keeps its place).  A tile that a
+    launch skipped or computed twice at some position would differ."""
+    cfg = get_config(key)
+    print(f"[fullsize] {key}: every matrix, forward and reversed batch order", flush=True)
+    results = []
+    for order in (list(range(cfg.count)), list(range(cfg.count))[::-1]):
+        data = make_set(cfg)
+        upd = [torch.empty(g.shape, device="cuda") for g in data["grads"]]
+
+        def pick(xs):
+            return [xs[i] for i in order]
+
+        step = nsa.MuonStep(pick(data["params"]), pick(data["grads"]), pick(data["momentum"]),
+                            ns_steps=cfg.ns_steps[0], mu=cfg.momentum, nesterov=cfg.nesterov, lr=cfg.lr,
+                            update_out=pick(upd))
+        step()
+        torch.cuda.synchronize()
+        results.append((upd, data["params"]))
+        del data, step
+    (u0, p0), (u1, p1) = results
+    for i, spec in enumerate(cfg.matrices):
+        assert torch.isfinite(u0[i]).all(), spec.name
+        assert torch.equal(u0[i], u1[i]), (i, spec.name)
+        assert torch.equal(p0[i], p1[i]), (i, spec.name)
+    del results, u0, u1, p0, p1
+    torch.cuda.empty_cache()
