@@ -175,6 +175,8 @@ def clock_sampler(path, parent):
                 clk = d.get("clock") or {}
                 rec["gfx_mhz"] = [m for k, v in sorted(clk.items()) if k.startswith("gfx_") and isinstance(v, dict)
                                   for m in [_mhz(v.get("clk"))] if m]
+                rec["mem_mhz"] = [m for k, v in sorted(clk.items()) if k.startswith("mem") and isinstance(v, dict)
+                                  for m in [_mhz(v.get("clk"))] if m]
                 power = d.get("power") or {}
                 rec["power_w"] = {k: float(v["value"]) for k, v in power.items()
                                   if isinstance(v, dict) and isinstance(v.get("value"), (int, float))}
@@ -221,6 +223,10 @@ def stop_clock_sampler(sampler, t0, t1):
     mean = [sum(r["gfx_mhz"]) / len(r["gfx_mhz"]) for r in inside]
     out = {"samples": len(inside), "gfx_clock_mhz_mean": sum(mean) / len(mean), "gfx_clock_mhz_min": min(mean),
            "gfx_clock_mhz_max": max(mean)}
+    mem = [sum(r["mem_mhz"]) / len(r["mem_mhz"]) for r in inside if r.get("mem_mhz")]
+    if mem:
+        out.update({"mem_clock_mhz_mean": sum(mem) / len(mem), "mem_clock_mhz_min": min(mem),
+                    "mem_clock_mhz_max": max(mem)})
     pw = [r.get("power_w", {}) for r in inside]
     for k in sorted(set().union(*pw)):
         vals = [p[k] for p in pw if k in p]
@@ -337,7 +343,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama3_8b")
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
