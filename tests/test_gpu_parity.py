@@ -400,3 +400,18 @@ def test_ns_rejects_bad_input():
         nsa.ns_batched([torch.randn(16, device="cuda")])
     with pytest.raises(TypeError):
         nsa.ns_batched([torch.randn(16, 16, device="cuda", dtype=torch.float16)])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_segments_of_whole_tile_rounds_and_a_tail(dtype):
+    """Shape groups large enough that the contraction launches hand their
+    tiles to the XCDs in whole rounds of 256 plus a ragged tail: five
+    2560 x 2560 matrices (500 update tiles, 275 lower-triangle Gram tiles) and
+    2560 x 5376 in both orientations (630 update tiles, 165 Gram tiles of
+    K = 5376).  Every matrix against the oracle."""
+    shapes = [(2560, 2560)] * 5 + [(5376, 2560), (2560, 5376), (5376, 2560)]
+    cfg = _adhoc(shapes, dtype, 220 + (dtype == "bf16"))
+    print(f"[parity] whole rounds + tail: {dtype} {shapes}", flush=True)
+    res = run_muon(cfg)
+    check_against_oracle(cfg, res)
