@@ -86,13 +86,20 @@ def coefficient_schedule(coeffs, steps: int) -> list:
 
 
 def newton_schulz(g, steps: int, coeffs=None) -> np.ndarray:
-    """Cubic Newton-Schulz orthogonalisation.
+    """Newton-Schulz orthogonalisation.
 
-    Blog post, section "Muon 核心：Newton-Schulz 迭代": G0 = G / ||G||_F, then
-    G_{t+1} = 1.5 G_t - 0.5 G_t G_t^T G_t, evaluated as two products per step
-    (A = G G^T, then A G).  Section "代码实现" (``newton_schulz``) fixes the
-    details: rows > cols is handled on the transpose so the Gram matrix is the
-    smaller side, and the norm gets +1e-7.
+    Blog post, section "Muon 核心：Newton-Schulz 迭代": the input is scaled to
+    unit Frobenius norm and then mapped ``steps`` times by the odd polynomial
+    G <- 1.5 G - 0.5 (G G^T) G, whose cost is two matrix products per step
+    (the Gram matrix A = G G^T, then A G).  The same section's implementation
+    notes fix three details: a matrix with more rows than columns is iterated
+    as its transpose (so A is the smaller square) and transposed back at the
+    end, and the norm in the scaling carries +1e-7.
+
+    ``coeffs`` replaces the cubic's (1.5, -0.5) by another odd polynomial
+    (training guide, ``ns_backend`` row): each step maps X to
+    sum_j c_j A^j X with A = X X^T, the powers formed by repeated products
+    A (A^(j-1) X).  The cubic is the case (c0, c1) = (1.5, -0.5).
     """
     g = _f64_2d(g)
     if steps < 0:
@@ -101,14 +108,6 @@ def newton_schulz(g, steps: int, coeffs=None) -> np.ndarray:
     transposed = rows > cols
     x = g.T if transposed else g
     x = x / (frobenius_norm(x) + EPS)
-    if coeffs is None:
-        for _ in range(steps):
-            a = x @ x.T
-            x = 1.5 * x - 0.5 * (a @ x)
-        return x.T if transposed else x
-    # Custom coefficients (training guide, ``ns_backend`` row): each step maps
-    # X to sum_j c_j A^j X with A = X X^T, the powers formed by repeated
-    # products A (A^(j-1) X).
     for c in coefficient_schedule(coeffs, steps):
         a = x @ x.T
         term = x

@@ -569,3 +569,38 @@ def pin_adamw_loops(adamw, seed=73):
 
 
 ADAMW_PINS = [pin_adamw_closed_forms, pin_adamw_loops]
+
+
+# ----------------------------------------------------------------------------- orthogonality error
+def pin_orthogonality_closed_form(orth, seed=79):
+    """Blog post, "调试技巧": the check is ||X X^T - I||_F.  For X = L diag(s) R^T
+    (L, R with orthonormal columns, r = min(rows, cols)) taken on its wide side,
+    X X^T - I = L diag(s^2 - 1) L^T on the range of L and -I on its complement,
+    so the error is sqrt(sum_i (s_i^2 - 1)^2 + (m' - r)) with m' the short side.
+    A flat spectrum s gives sqrt(r) |1 - s^2|; a spectrum that mixes values
+    above and below 1 separates the Frobenius norm from the spectral norm and
+    from sums that drop the square."""
+    rng = np.random.default_rng(seed)
+    for r, n in ((4, 9), (16, 40), (64, 256)):
+        q = haar_orthonormal(rng, n, r).T                    # r x n, orthonormal rows
+        for s in (0.0, 0.25, 0.9, 1.0, 1.7):
+            want = math.sqrt(r) * abs(1.0 - s * s)
+            for x in (s * q, s * q.T):                       # wide and tall orientation
+                got = float(orth(x))
+                assert abs(got - want) <= 1e-12 * max(1.0, want), (r, n, s, got, want)
+    for rows, cols in ((6, 20), (20, 6), (12, 12)):
+        r = min(rows, cols)
+        sigma = np.linspace(0.2, 1.8, r)
+        x, _, _ = _spectral_case(rng, rows, cols, sigma)
+        want = math.sqrt(float(np.sum((sigma * sigma - 1.0) ** 2)))
+        got = float(orth(x))
+        assert abs(got - want) <= 1e-12 * want, (rows, cols, got, want)
+    # rank-deficient wide input: the missing directions each contribute 1
+    left = haar_orthonormal(rng, 8, 5)
+    right = haar_orthonormal(rng, 30, 5)
+    x = left @ right.T                                       # 8 x 30, rank 5, unit singular values
+    got = float(orth(x))
+    assert abs(got - math.sqrt(3.0)) <= 1e-12, got
+
+
+ORTH_PINS = [pin_orthogonality_closed_form]

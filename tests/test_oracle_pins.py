@@ -118,6 +118,11 @@ def test_single_step_nesterov_from_zero_is_scaled_grad():
     assert norms[0] == pytest.approx(1.95 * np.linalg.norm(g), rel=1e-14)
 
 
+@pytest.mark.parametrize("pin", _pins.ORTH_PINS, ids=lambda f: f.__name__)
+def test_orthogonality_error_pin(pin):
+    pin(oracle.orthogonality_error)
+
+
 def test_orthogonality_error_uses_wide_side():
     rng = np.random.default_rng(2)
     x = oracle.newton_schulz(rng.standard_normal((12, 4)), 40)

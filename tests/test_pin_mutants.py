@@ -255,3 +255,42 @@ def test_unmutated_adamw_copy_passes(golden):
     _pins.pin_adamw_worked_example(_adamw_factory(), golden("adamw_worked_example.txt"))
     for pin in _pins.ADAMW_PINS:
         pin(_adamw_factory())
+
+
+# ----------------------------------------------------------------------------- orthogonality error
+def _orth_factory(kind=None):
+    def orth(x):
+        x = np.asarray(x, dtype=np.float64)
+        if kind != "tall_side" and x.shape[0] > x.shape[1]:
+            x = x.T
+        if kind == "zero":
+            return 0.0
+        if kind == "gram_other_side":
+            d = x.T @ x - np.eye(x.shape[1])
+        else:
+            d = x @ x.T - np.eye(x.shape[0])
+        if kind == "spectral":
+            return float(np.linalg.norm(d, 2))
+        if kind == "no_square":
+            return float(np.sum(np.abs(d)))
+        if kind == "singular_values":
+            return float(np.linalg.norm(np.linalg.svd(x, compute_uv=False) - 1.0))
+        return float(np.sqrt(np.sum(d * d)))
+    return orth
+
+
+ORTH_MUTANTS = {k: _orth_factory(k) for k in ("zero", "tall_side", "gram_other_side", "spectral", "no_square",
+                                              "singular_values")}
+
+
+@pytest.mark.parametrize("name", sorted(ORTH_MUTANTS))
+def test_orthogonality_mutant_is_caught(name):
+    caught = False
+    for pin in _pins.ORTH_PINS:
+        caught = caught or _caught(lambda: pin(ORTH_MUTANTS[name]))
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_orthogonality_copy_passes():
+    for pin in _pins.ORTH_PINS:
+        pin(_orth_factory())
