@@ -111,9 +111,13 @@ typedef struct {
 
 /*
  * Workspace size for dmuon_ns_batched over the given shapes and configuration
- * (NULL = default), in bytes.  Writes *bytes_out and returns DMUON_OK, or an
- * argument error.  Needs no GPU.  A three-term polynomial needs an extra
- * m' x m' buffer per matrix.
+ * (NULL = default), in bytes.  The blog post's "什么时候用 / 不用？" notes that
+ * Newton-Schulz needs temporary matrices; here they are the iterate (two
+ * operand copies plus, for bf16, its low half) and the m' x m' Gram matrix per
+ * matrix, in the caller's workspace.  Writes *bytes_out and returns DMUON_OK,
+ * or an argument error (the shape rules of dmuon_ns_batched, whose
+ * newton_schulz in "代码实现" accepts 2-D matrices only).  Needs no GPU.  A
+ * three-term polynomial needs an extra m' x m' buffer per matrix.
  */
 int dmuon_ns_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
                              const dmuon_ns_config* ns_config, size_t* bytes_out);
@@ -143,7 +147,10 @@ int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out,
 
 /*
  * Workspace size for dmuon_muon_step over the given shapes and Newton-Schulz
- * configuration (NULL = default), in bytes.  Needs no GPU.
+ * configuration (NULL = default), in bytes: the Newton-Schulz temporaries of
+ * the matrices that take that route (blog post, "什么时候用 / 不用？"; matrices
+ * below DMUON_MIN_NS_NUMEL need none), plus descriptors and the per-block norm
+ * partials.  Same errors as dmuon_ns_workspace_bytes.  Needs no GPU.
  */
 int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
                                     const dmuon_ns_config* ns_config, size_t* bytes_out);
@@ -174,6 +181,11 @@ int dmuon_muon_step_workspace_bytes(int count, const int64_t* rows, const int64_
  *                 ||Y_i||_F.
  * params, grads, momentum and non-NULL update_out entries must be distinct
  * non-overlapping buffers.
+ * Range: the 1/(||Y|| + 1e-7) scale is folded into the first Newton-Schulz
+ * step, whose Gram product accumulates the unnormalised Y Y^T in fp32.  A
+ * matrix with ||Y||_F >= 2^63 (about 9.2e18; its norms_out entry may be inf)
+ * is outside that range and gets a NaN update, as a non-finite gradient does;
+ * the other matrices of the call are unaffected.
  */
 int dmuon_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
                     const int64_t* rows, const int64_t* cols, int dtype,
@@ -252,7 +264,11 @@ int dmuon_adamw_step(int count, void* const* params, const void* const* grads, f
                      float beta2, float eps, float weight_decay, void* workspace, size_t workspace_bytes,
                      void* hip_stream);
 
-/* Static text for a status code. */
+/* Static text for a status code.  The codes translate the pages' error
+ * conventions to return values: the blog's newton_schulz asserts a 2-D input
+ * ("代码实现", and "常见错误" 2: a bias vector must not reach NS) and accepts
+ * float32 or bfloat16 only; the training guide's optimizer rejects bad
+ * parameter lists when it is built ("第 4 步：创建优化器"). */
 const char* dmuon_status_string(int status);
 
 /* Details of the last error returned on the calling thread ("" if none). */

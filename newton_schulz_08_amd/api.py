@@ -129,6 +129,19 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _used_on(stream, *tensors) -> None:
+    """Buffers allocated here come from the caching allocator's pool of the
+    current stream.  When the kernels that use them run on another stream,
+    record that stream, or the block could be handed to a new allocation on
+    the current stream as soon as this function drops its reference, while
+    the kernels still read and write it."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None and stream.cuda_stream != torch.cuda.current_stream(t.device).cuda_stream:
+            t.record_stream(stream)
+
+
 def ns_batched(xs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]] = None, ns_steps: int = 5,
                workspace: Optional[torch.Tensor] = None, stream=None, ns_coeffs=None,
                ns_backend: str = "gram") -> List[torch.Tensor]:
@@ -139,7 +152,8 @@ def ns_batched(xs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]
     dt = xs[0].dtype
     for i, x in enumerate(xs):
         _check_matrix(x, f"xs[{i}]", dt)
-    if outs is None:
+    own_outs = outs is None
+    if own_outs:
         outs = [torch.empty_like(x) for x in xs]
     for i, (o, x) in enumerate(zip(outs, xs)):
         _check_matrix(o, f"outs[{i}]", dt)
@@ -148,13 +162,15 @@ def ns_batched(xs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]
     shapes = [tuple(x.shape) for x in xs]
     cfg = ns_config(ns_coeffs, ns_backend, int(ns_steps))
     need = ns_workspace_bytes(shapes, dt, ns_coeffs, ns_backend)
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = alloc_workspace(need, xs[0].device)
     rows, cols = _shape_arrays(shapes)
     check(_lib.load().dmuon_ns_batched(len(xs), _ptrs(xs), _ptrs(outs), rows, cols, dtype_code(dt), int(ns_steps),
                                        _cfg_ptr(cfg), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                        ctypes.c_void_p(_stream_handle(stream))),
           "dmuon_ns_batched")
+    _used_on(stream, workspace if own_ws else None, *(outs if own_outs else ()))
     return list(outs)
 
 
@@ -214,6 +230,7 @@ class MuonStep:
         self._scale_mode = modes[lr_scale_mode]
         self._cfg = ns_config(ns_coeffs, ns_backend, self.ns_steps)
         self.workspace_bytes = muon_step_workspace_bytes(self.shapes, dt, ns_coeffs, ns_backend)
+        self._own_ws = workspace is None
         self.workspace = workspace if workspace is not None else alloc_workspace(self.workspace_bytes,
                                                                                  params[0].device)
         if self.workspace.numel() < self.workspace_bytes:
@@ -227,6 +244,8 @@ class MuonStep:
             ctypes.c_float(self.lr), ctypes.c_float(self.weight_decay), self._scale_mode,
             self._scale, self._upd, self._norms, ctypes.c_void_p(self.workspace.data_ptr()),
             self.workspace.numel(), ctypes.c_void_p(_stream_handle(stream))), "dmuon_muon_step")
+        if self._own_ws:
+            _used_on(stream, self.workspace)
 
 
 def muon_step(params, grads, momentum, **kw) -> None:
@@ -267,13 +286,15 @@ def clip_grad_norm_(grads: Sequence[torch.Tensor], max_norm, segments: Optional[
     mn = (ctypes.c_float * nseg)(*max_norms)
     totals = torch.empty(nseg, dtype=torch.float32, device=grads[0].device)
     need = clip_grad_norm_workspace_bytes([g.numel() for g in grads], nseg)
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = alloc_workspace(need, grads[0].device)
     check(_lib.load().dmuon_clip_grad_norm(n, _ptrs(grads), numel, dtype_code(dt), segarr, nseg, mn,
                                            ctypes.c_float(norm_type), ctypes.c_void_p(totals.data_ptr()),
                                            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                            ctypes.c_void_p(_stream_handle(stream))),
           "dmuon_clip_grad_norm")
+    _used_on(stream, totals, workspace if own_ws else None)
     return totals
 
 
@@ -307,7 +328,8 @@ def adamw_step_(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], e
                 raise ValueError(f"{name}[{i}] has {t.numel()} elements, params[{i}] has {params[i].numel()}")
     numels = [p.numel() for p in params]
     numel = (ctypes.c_int64 * n)(*numels)
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = alloc_workspace(adamw_step_workspace_bytes(numels), params[0].device)
     b1, b2 = betas
     check(_lib.load().dmuon_adamw_step(n, _ptrs(params), _ptrs(grads), _ptrs(exp_avg), _ptrs(exp_avg_sq), numel,
@@ -316,6 +338,8 @@ def adamw_step_(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], e
                                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                        ctypes.c_void_p(_stream_handle(stream))),
           "dmuon_adamw_step")
+    # AdamWStep passes its own workspace and keeps it
+    _used_on(stream, workspace if own_ws else None)
 
 
 class AdamWStep:
@@ -337,6 +361,7 @@ class AdamWStep:
         self.step += 1
         adamw_step_(self.params, self.grads, self.exp_avg, self.exp_avg_sq, self.step, self.lr, self.betas,
                     self.eps, self.weight_decay, self.workspace, stream)
+        _used_on(stream, self.workspace, *self.exp_avg, *self.exp_avg_sq)
 
 
 def backend_info() -> str:

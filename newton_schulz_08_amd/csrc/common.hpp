@@ -27,6 +27,9 @@ constexpr int kEwRowTileRows = 16;   // elementwise tile of every other matrix: 
 constexpr int kEwRowTileCols = 256;
 constexpr int kEwThreads = 256;
 constexpr float kNormEps = 1e-7f;    // blog post: G / (G.norm() + 1e-7)
+// Largest ||Y||_F whose scale can be folded into the first Newton-Schulz step
+// in fp32 (||Y||^2 and 1 / ||Y||^2 both normal floats).
+constexpr float kMaxFoldedNorm = 9223372036854775808.0f;   // 2^63
 
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
 

@@ -214,7 +214,8 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
   pl.off_prefix = off;
   off = align_up(off + sizeof(int) * (count + 1));
   pl.off_partials = off;
-  off = align_up(off + sizeof(float) * std::max(tiles, 1));
+  // four 16 x 64 block partials of the sum of squares per prologue tile
+  off = align_up(off + sizeof(float) * 4 * static_cast<size_t>(std::max(tiles, 1)));
   pl.off_scales = off;
   off = align_up(off + sizeof(MatScale) * count);
   const size_t eb = elem_bytes(dt);
@@ -453,7 +454,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
                            call.nesterov, call.lr, call.decay, ew_grid, stream);
   });
   if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
-  e = timed(kKNorm, 0.0, 4.0 * pl.total_tiles, stream, [&] {
+  e = timed(kKNorm, 0.0, 16.0 * pl.total_tiles, stream, [&] {
     return launch_norm_finalize(d_descs, d_prefix, pl.count, d_partials, d_scales, call.norms_out, stream);
   });
   if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("norm launch: ") + hipGetErrorString(e));
@@ -778,12 +779,19 @@ int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out, con
   return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
-int dmuon_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
-                    const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
-                    const dmuon_ns_config* ns_config, float mu, int nesterov, float lr, float weight_decay,
-                    int lr_scale_mode, const float* lr_scale, float* const* update_out, float* norms_out,
-                    void* workspace, size_t workspace_bytes, void* hip_stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace dmuon {
+namespace {
+
+// Validates the arguments of a Muon step and builds its plan and call record
+// (everything but the workspace).  DMUON_OK with *empty set means count == 0.
+int prepare_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
+                      const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
+                      const dmuon_ns_config* ns_config, float mu, int nesterov, float lr, float weight_decay,
+                      int lr_scale_mode, const float* lr_scale, float* const* update_out, float* norms_out,
+                      Plan* plan, Call* call_out, bool* empty) {
+  *empty = false;
   int st = validate_shapes(count, rows, cols, dtype);
   if (st != DMUON_OK) return st;
   if (ns_steps < 0 || ns_steps > DMUON_MAX_NS_STEPS)
@@ -794,7 +802,10 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
     return fail(DMUON_ERR_INVALID_ARG, "lr_scale_mode must be DMUON_LR_SCALE_ONE or DMUON_LR_SCALE_MOONLIGHT");
   NsCfg ns;
   if ((st = resolve_ns_config(ns_config, ns_steps, true, &ns)) != DMUON_OK) return st;
-  if (count == 0) return DMUON_OK;
+  if (count == 0) {
+    *empty = true;
+    return DMUON_OK;
+  }
   if ((st = check_ptr_array(count, reinterpret_cast<const void* const*>(params), "params", false)) != DMUON_OK)
     return st;
   if ((st = check_ptr_array(count, grads, "grads", false)) != DMUON_OK) return st;
@@ -812,9 +823,7 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
     if (update_out) ptrs.push_back({update_out[i], "update_out" + s});
   }
   if ((st = check_distinct(ptrs)) != DMUON_OK) return st;
-  const Plan pl = make_plan(count, rows, cols, dtype, true, ns.terms == 3);
-  if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
-  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
+  *plan = make_plan(count, rows, cols, dtype, true, ns.terms == 3);
   Call call{};
   call.mode = kModeMuon;
   call.in = grads;
@@ -831,6 +840,29 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
   call.decay = static_cast<float>(1.0 - static_cast<double>(lr) * static_cast<double>(weight_decay));
   call.nesterov = nesterov ? 1 : 0;
   call.ns = ns;
+  *call_out = call;
+  return DMUON_OK;
+}
+
+}  // namespace
+}  // namespace dmuon
+
+extern "C" {
+
+int dmuon_muon_step(int count, void* const* params, const void* const* grads, float* const* momentum,
+                    const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
+                    const dmuon_ns_config* ns_config, float mu, int nesterov, float lr, float weight_decay,
+                    int lr_scale_mode, const float* lr_scale, float* const* update_out, float* norms_out,
+                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_last_error.clear();
+  Plan pl;
+  Call call{};
+  bool empty = false;
+  int st = prepare_muon_step(count, params, grads, momentum, rows, cols, dtype, ns_steps, ns_config, mu, nesterov,
+                             lr, weight_decay, lr_scale_mode, lr_scale, update_out, norms_out, &pl, &call, &empty);
+  if (st != DMUON_OK || empty) return st;
+  if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
+  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
   return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
 }
 

@@ -4,7 +4,7 @@
 //   tiles; 64 x 64 for tall Newton-Schulz matrices):
 //     buf <- mu * buf + g                       (blog post VanillaMuon: mul_ then add_)
 //     Y   <- g + mu * buf  or  buf              (training guide: nesterov ns_input)
-//     partial sum of Y^2 per tile               (Frobenius norm of the NS input)
+//     partial sums of Y^2 per 16 x 64 block     (Frobenius norm of the NS input)
 //   small matrices (numel < 100000, training guide "编写 Predicate"):
 //     p <- p (1 - lr wd) - lr * s * Y, update_out <- Y  (blog VanillaMuon non-matrix
 //     branch, with the decoupled weight decay of the training guide's optimizer)
@@ -14,7 +14,16 @@
 //   both sides stay coalesced.
 //   The 1/||Y|| scale is folded into the first Newton-Schulz step instead of a
 //   second pass.
-// norm_finalize_kernel -- fixed-order sum of each matrix's tile partials.
+// norm_finalize_kernel -- fixed-order sum of each matrix's block partials.
+//
+// The sum of squares is reduced in one canonical order over the wide
+// orientation, whatever tile shape produced the values: the wide iterate
+// (Mp x Np) is cut into 16-row x 64-column blocks; a block's partial is the sum
+// over its 16 rows (fixed pairwise tree) of row sums, each row sum a 16-lane
+// butterfly over four-element quads, each quad an fmaf chain in column order.
+// Block partials are stored row-major over the block grid.  A matrix and its
+// transpose therefore get bitwise the same norm, and since their iterates are
+// the same wide matrix, bitwise the same Newton-Schulz result.
 // apply_x0_kernel -- ns_steps == 0 only: U = Y / (||Y|| + eps) to the caller.
 #include <hip/hip_runtime.h>
 
@@ -115,6 +124,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over the 16 lanes of an aligned lane group (every lane gets the same
+// value: each butterfly level adds the same two operands in either order).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum of squares of a four-element quad, in column order.
+__device__ __forceinline__ float quad_ss(const float (&y)[4]) {
+  float q = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) q = fmaf(y[e], y[e], q);
+  return q;
+}
+
+// A block's 16 row sums, added in a fixed pairwise tree.
+__device__ __forceinline__ float block_sum(const float* r) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = r[2 * i] + r[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
 // Tile shapes (4096 elements, 256 threads, four passes of four elements per
 // thread).  A tall Newton-Schulz matrix is written transposed, so its tiles
 // are 64 x 64 and go through LDS; every other matrix uses 16 x 256 tiles, in
@@ -134,8 +169,9 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
                                                               float decay) {
   using T = typename Elem<DT>::T;
   __shared__ float tile[kEwTile][kEwTile + 1];
-  __shared__ float red[kEwThreads / 64];
+  __shared__ float rowsum[4][16];   // row sums of the tile's four 16 x 64 blocks
   const int tid = threadIdx.x;
+  const int quad = tid & 15;        // four-element quad within a block row
 
   for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
     const MatDesc& d = descs[find_matrix(prefix, nmat, t)];
@@ -150,7 +186,6 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
     const int rstep = kEwThreads / sh.tpr;
     const int np = d.np;
     const float step_lr = -lr * d.lr_scale;
-    float ss = 0.0f;
 
     // every load of the tile first, then the arithmetic and the stores
     float g[4][4], b[4][4], pv[4][4];
@@ -197,22 +232,24 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
           if (d.upd) store4(d.upd + o[pass], vec[pass], valid[pass], y);
         }
       }
+      if (ns && trn) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ss = fmaf(y[e], y[e], ss);
-      if (ns) {
-        // the covered extent is padded to 256, so every tile position exists
-        if (!trn) {
-          // wide: caller rows are rows of X
-          store_iterate<DT>(d, static_cast<long>(r) * np + c, y);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) tile[rl][cl + e] = y[e];
-        }
+        for (int e = 0; e < 4; ++e) tile[rl][cl + e] = y[e];
+      } else {
+        // 16 x 256 tile in the wide orientation: block (tid >> 4) & 3, block row rl
+        const float rs = row16_sum(quad_ss(y));
+        if (quad == 0) rowsum[(tid >> 4) & 3][rl] = rs;
+        // the covered extent is padded to 256, so every tile position exists;
+        // wide: caller rows are rows of X
+        if (ns) store_iterate<DT>(d, static_cast<long>(r) * np + c, y);
       }
     }
 
+    long pidx;   // the tile's first block partial; its blocks follow at stride bstride
+    int bstride;
     if (ns && trn) {
-      // tall: caller columns are rows of X, written through the LDS tile
+      // tall: caller columns are rows of X, written through the LDS tile.
+      // Pass p is block p of the tile's 64 wide rows, block row rl0.
       __syncthreads();
 #pragma unroll
       for (int pass = 0; pass < 4; ++pass) {
@@ -220,14 +257,23 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = tile[cl + e][j];
+        const float rs = row16_sum(quad_ss(v));
+        if (quad == 0) rowsum[pass][rl0] = rs;
         store_iterate<DT>(d, static_cast<long>(c0 + j) * np + r0 + cl, v);
       }
+      // wide block grid (Mp / 16) x (Np / 64): this tile is block column
+      // r0 / 64 of block rows c0 / 16 .. c0 / 16 + 3
+      const int bcols = d.ew_rows / kEwTile;
+      pidx = static_cast<long>(c0 / 16) * bcols + r0 / kEwTile;
+      bstride = bcols;
+    } else {
+      // wide block grid (rows / 16) x (cols / 64): block row r0 / 16, block
+      // columns c0 / 64 .. c0 / 64 + 3, i.e. 4 local .. 4 local + 3
+      pidx = 4L * local;
+      bstride = 1;
     }
-
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
-    if (tid == 0) partials[t] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (tid < 4) partials[4L * d.ew_tile0 + pidx + static_cast<long>(tid) * bstride] = block_sum(rowsum[tid]);
     __syncthreads();
   }
 }
@@ -239,16 +285,21 @@ __global__ __launch_bounds__(kEwThreads) void norm_finalize_kernel(const MatDesc
                                                                    float* __restrict__ norms_out) {
   __shared__ float red[kEwThreads / 64];
   const int i = blockIdx.x;
-  const int t0 = prefix[i], t1 = prefix[i + 1];
+  const long t0 = 4L * prefix[i], t1 = 4L * prefix[i + 1];   // four block partials per tile
   float s = 0.0f;
-  for (int t = t0 + threadIdx.x; t < t1; t += kEwThreads) s += partials[t];
+  for (long t = t0 + threadIdx.x; t < t1; t += kEwThreads) s += partials[t];
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
     const float ss = (red[0] + red[1]) + (red[2] + red[3]);
     const float norm = sqrtf(ss);
-    const float c = 1.0f / (norm + kNormEps);
+    // The scale is folded into the first Newton-Schulz step: its Gram product
+    // accumulates the unnormalised Y Y^T in fp32 and multiplies by c^2.  Both
+    // stay in range (entries below ||Y||^2, c^2 at least the smallest normal
+    // float) while ||Y|| < 2^63; beyond that (or an overflowed sum) the scale
+    // is NaN, so the matrix's update is NaN as for a non-finite gradient.
+    const float c = norm < kMaxFoldedNorm ? 1.0f / (norm + kNormEps) : __builtin_nanf("");
     MatScale sc;
     sc.c = c;
     sc.c2 = c * c;

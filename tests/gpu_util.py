@@ -75,3 +75,21 @@ def max_ulp_err_f32(gpu: np.ndarray, exact: np.ndarray) -> float:
 
 def fmt(x: float) -> str:
     return f"{x:.3e}" if not math.isnan(x) else "nan"
+
+
+def worst_tile_error(got: np.ndarray, want: np.ndarray, tile: int = 256):
+    """Largest relative Frobenius error over the tile x tile blocks of a
+    matrix (ragged edge blocks included), with that block's (row, col) index.
+    A single wrong contraction tile barely moves the whole-matrix error of a
+    large matrix; it dominates its own block's."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    worst, where = 0.0, (0, 0)
+    for bi in range(0, want.shape[0], tile):
+        for bj in range(0, want.shape[1], tile):
+            w = want[bi:bi + tile, bj:bj + tile]
+            den = float(np.linalg.norm(w))
+            err = float(np.linalg.norm(got[bi:bi + tile, bj:bj + tile] - w)) / (den if den > 0 else 1.0)
+            if not err <= worst:   # NaN counts as worst
+                worst, where = err, (bi // tile, bj // tile)
+    return worst, where

@@ -74,28 +74,28 @@ def _cfg(backend=0, terms=0, per_step=0, coeffs=()):
 
 
 def test_workspace_layout_exact(lib):
-    # one 512x2048 fp32 matrix: descriptor 128 B, prefix 8 B, 256 prologue
-    # tiles (1 KB), scales 16 B -- each region 256-aligned -- then the fp32
-    # iterate in two buffers that alternate between steps, and A
-    # iterate in two buffers that alternate between steps, and A; m' = 512 is
+    # one 512x2048 fp32 matrix: descriptor 128 B, prefix 8 B, the sum-of-squares
+    # partials of its 16 x 64 blocks (1024 blocks, 4 KB), scales 16 B -- each
+    # region 256-aligned -- then the fp32 iterate in two buffers that
+    # alternate between steps, and A; m' = 512 is
     # two tile rows, so the Gram's K = 2048 is cut into 8 slices whose fp32
     # 256x256 partial products (sized for all 2 x 2 tiles) follow
     st, nbytes = _ws(lib, [(512, 2048)], dt=0)
     assert st == 0
     mb = 512 * 2048 * 4
     part = 2 * 2 * 8 * 256 * 256 * 4
-    assert nbytes == 256 + 256 + 1024 + 256 + 2 * mb + 512 * 512 * 4 + part
+    assert nbytes == 256 + 256 + 4096 + 256 + 2 * mb + 512 * 512 * 4 + part
     # bf16: the iterate's low half + two operand copies (its high half, one per
     # step parity) + bf16 Gram
     st, nb16 = _ws(lib, [(512, 2048)], dt=1)
-    assert nb16 == 256 + 256 + 1024 + 256 + 512 * 2048 * (2 + 2 + 2) + 512 * 512 * 2 + part
+    assert nb16 == 256 + 256 + 4096 + 256 + 512 * 2048 * (2 + 2 + 2) + 512 * 512 * 2 + part
     # a three-term polynomial adds the m' x m' buffer B = c1 A + c2 A^2 (its
     # square product, K = 512 in 2 slices, shares the partial products)
     st, nb3 = _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(terms=3, coeffs=(3.4445, -4.775, 2.0315)))
     assert st == 0 and nb3 == nb16 + 512 * 512 * 2
     # three tile rows or more: no slices, no partial products
     st, big = _ws(lib, [(768, 2048)], dt=0)
-    assert big == 256 + 256 + (768 // 16) * (2048 // 256) * 4 + 256 + 2 * 768 * 2048 * 4 + 768 * 768 * 4
+    assert big == 256 + 256 + (768 // 16) * (2048 // 64) * 4 + 256 + 2 * 768 * 2048 * 4 + 768 * 768 * 4
     # two terms or another backend need nothing extra
     assert _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(terms=2, coeffs=(1.5, -0.5)))[1] == nb16
     assert _ws(lib, [(512, 2048)], dt=1, cfg=_cfg(backend=1))[1] == nb16

@@ -12,7 +12,8 @@ import newton_schulz_08_amd as nsa
 from workloads import gen, get_config
 from workloads.device import make_set
 
-from gpu_util import (TOL, check_update_faithful, f32_mu, max_ulp_err_f32, rel_fro, to_device, to_host_f64)
+from gpu_util import (TOL, check_update_faithful, f32_mu, max_ulp_err_f32, rel_fro, to_device, to_host_f64,
+                      worst_tile_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,8 +53,11 @@ def run_set(key, sample, ns_steps):
         else:
             err = rel_fro(u, uw[0])
             worst = max(worst, err)
-            print(f"[fullsize] {key} {spec.name} {spec.rows}x{spec.cols}: rel err {err:.3e}", flush=True)
+            terr, tij = worst_tile_error(u, uw[0])
+            print(f"[fullsize] {key} {spec.name} {spec.rows}x{spec.cols}: rel err {err:.3e}, worst 256x256 tile "
+                  f"{tij} {terr:.3e}", flush=True)
             assert err <= TOL[cfg.dtype], (spec.name, err)
+            assert terr <= TOL[cfg.dtype], (spec.name, tij, terr)
         check_update_faithful(to_host_f64(data["params"][i]), dw.as_f64(), u, cfg.lr, 1.0, cfg.dtype)
         assert abs(norms[i].item() - nw[0]) <= 1e-5 * nw[0]
     del data, step
@@ -107,8 +111,11 @@ def test_spectrum_set_all_steps(dtype):
         worst = 0.0
         for i, (d, o) in enumerate(zip(ins, outs)):
             u = to_host_f64(o)
-            err = rel_fro(u, oracle.newton_schulz(d.as_f64(), k))
+            want = oracle.newton_schulz(d.as_f64(), k)
+            err = rel_fro(u, want)
             assert err <= TOL[dtype], (i, k, err)
+            terr, tij = worst_tile_error(u, want)
+            assert terr <= TOL[dtype], (i, k, tij, terr)
             worst = max(worst, err)
             errs.setdefault(i, []).append(oracle.orthogonality_error(u))
         print(f"spectrum set {dtype} k={k}: worst relative Frobenius error {worst:.3e}", flush=True)

@@ -12,7 +12,7 @@ from workloads import gen
 from workloads.configs import MatrixSpec, SetConfig, get_config
 
 from gpu_util import (TOL, TORCH_DT, check_update_faithful, f32_mu, gpu_lr_scale, max_ulp_err_f32, rel_fro,
-                      to_device, to_host_f64, ulp)
+                      to_device, to_host_f64, ulp, worst_tile_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +88,8 @@ def check_against_oracle(cfg, res, *, ns_steps=5, mu=0.95, nesterov=True, lr=0.0
                 err = rel_fro(u, uw[0])
                 worst = max(worst, err)
                 assert err <= TOL[dtype], f"{spec.name} {spec.rows}x{spec.cols}: rel err {err:.3e} > {TOL[dtype]}"
+                terr, tij = worst_tile_error(u, uw[0])
+                assert terr <= TOL[dtype], f"{spec.name} {spec.rows}x{spec.cols}: tile {tij} rel err {terr:.3e}"
             check_update_faithful(res["p"][i], res["p0"][i], u, lr, gpu_lr_scale(s, spec.rows, spec.cols, moonlight),
                                   dtype, weight_decay)
     return worst
@@ -415,3 +417,180 @@ def test_segments_of_whole_tile_rounds_and_a_tail(dtype):
     print(f"[parity] whole rounds + tail: {dtype} {shapes}", flush=True)
     res = run_muon(cfg)
     check_against_oracle(cfg, res)
+
+
+# ------------------------------------------------------------------ scale, transpose, many shape groups
+def _half_ulp_f32(x: float) -> float:
+    return float(np.spacing(np.float32(x))) / 2.0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_power_of_two_scaling(dtype):
+    """Blog post, "常见错误" 1: Newton-Schulz needs the normalisation, or large
+    norms blow up.  Gradients scaled by 2^k, k in {-40, -20, 0, 20, 40}, one
+    Llama-3-8B k_proj shape (1024 x 4096) and one TinyMLP gate shape
+    (2048 x 512, tall): every update meets the oracle.  Scaling by a power of
+    two is exact in every fp32/bf16 operation of the path (no value leaves the
+    normal range), so for every k at which the +1e-7 of the norm is below
+    half an ulp of the norm (it then cannot change the rounded sum) the update
+    and parameters must be bitwise the same.  That holds at k = 20 and 40 for
+    both shapes, and at k = 0 where the norm is large enough."""
+    shapes = [(1024, 4096), (2048, 512)]
+    cfg = _adhoc(shapes, dtype, 230 + (dtype == "bf16"), grad_scale=1e-3 if dtype == "bf16" else 1.0)
+    g = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(2)]
+    p0 = [gen.draw_matrix(cfg, i, gen.WEIGHT) for i in range(2)]
+    exact = {0: [], 1: []}   # per matrix: (k, update, params) where the epsilon is negligible
+    for k in (0, -40, -20, 20, 40):
+        dg = [to_device(x) * (2.0 ** k) for x in g]
+        dp = [to_device(x) for x in p0]
+        db = [torch.zeros(s, device="cuda") for s in shapes]
+        du = [torch.empty(s, device="cuda") for s in shapes]
+        norms = torch.empty(2, device="cuda")
+        nsa.muon_step(dp, dg, db, update_out=du, norms_out=norms)
+        torch.cuda.synchronize()
+        nrm = norms.cpu().tolist()
+        for i in range(2):
+            gh = to_host_f64(dg[i])
+            assert np.array_equal(gh, g[i].as_f64() * 2.0 ** k)      # the scaling itself was exact
+            _, _, uw, nw = oracle.muon_step([p0[i].as_f64()], [gh], [np.zeros(shapes[i])], f32_mu(0.95), True, 5,
+                                            0.02)
+            u = to_host_f64(du[i])
+            err = rel_fro(u, uw[0])
+            print(f"[scale] {dtype} 2^{k} {shapes[i]}: norm {nrm[i]:.4e}, rel err {err:.3e}", flush=True)
+            assert err <= TOL[dtype], (k, shapes[i], err)
+            assert abs(nrm[i] - nw[0]) <= 1e-5 * nw[0]
+            if 1e-7 < _half_ulp_f32(nrm[i]):
+                exact[i].append((k, du[i], dp[i]))
+    for i in range(2):
+        ks = [k for k, _, _ in exact[i]]
+        assert 20 in ks and 40 in ks, (shapes[i], ks)
+        k0, u0, p0_ = exact[i][0]
+        for k, u, pp in exact[i][1:]:
+            assert torch.equal(u, u0), (shapes[i], k0, k)
+            assert torch.equal(pp, p0_), (shapes[i], k0, k)
+
+
+def test_norm_beyond_folded_range_gives_nan():
+    """The 1/||Y|| scale is folded into the first Gram product, which needs
+    ||Y||^2 and 1/||Y||^2 to be normal floats: ||Y|| < 2^63.  A matrix beyond
+    that gets a NaN update (as a non-finite gradient does) instead of a
+    silently wrong one, and the rest of its batch is bitwise unchanged."""
+    shapes = [(512, 768), (768, 512)]
+    cfg = _adhoc(shapes, "f32", 232)
+    g = [to_device(gen.draw_matrix(cfg, i, gen.GRAD)) for i in range(2)]
+    p = [to_device(gen.draw_matrix(cfg, i, gen.WEIGHT)) for i in range(2)]
+    g[0] = g[0] * 2.0 ** 60                      # ||Y|| ~ 1.95 * 627 * 2^60 > 2^63
+    pa = [t.clone() for t in p]
+    u = [torch.zeros(s, device="cuda") for s in shapes]
+    norms = torch.empty(2, device="cuda")
+    nsa.muon_step(pa, g, [torch.zeros(s, device="cuda") for s in shapes], update_out=u, norms_out=norms)
+    pb = p[1].clone()
+    ub = torch.zeros(shapes[1], device="cuda")
+    nsa.muon_step([pb], [g[1]], [torch.zeros(shapes[1], device="cuda")], update_out=[ub])
+    torch.cuda.synchronize()
+    assert not norms[0].item() < 2.0 ** 63
+    assert torch.isnan(u[0]).all()
+    assert torch.equal(u[1], ub) and torch.equal(pa[1], pb)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_transpose_gives_bitwise_transposed_result(dtype):
+    """Blog post, "代码实现": a matrix with more rows than columns is iterated
+    as its transpose and transposed back, so NS(G^T) = NS(G)^T.  Both run on
+    the same wide iterate here, and the norm is summed in one order over the
+    wide orientation whatever the caller's layout, so the results are bitwise
+    transposes of each other: through ns_batched, and through the Muon step
+    (update, parameters, momentum, norm)."""
+    shapes = [(300, 700), (520, 1030), (1024, 4096), (256, 2304)]
+    cfg = _adhoc(shapes, dtype, 234 + (dtype == "bf16"))
+    g = [to_device(gen.draw_matrix(cfg, i, gen.GRAD)) for i in range(len(shapes))]
+    gt = [x.t().contiguous() for x in g]
+    outs = nsa.ns_batched(g, ns_steps=5)
+    outs_t = nsa.ns_batched(gt, ns_steps=5)
+    torch.cuda.synchronize()
+    for x, o, ot, s in zip(g, outs, outs_t, shapes):
+        assert torch.equal(ot, o.t()), s
+        assert rel_fro(to_host_f64(o), oracle.newton_schulz(to_host_f64(x), 5)) <= TOL[dtype], s
+    p = [to_device(gen.draw_matrix(cfg, i, gen.WEIGHT)) for i in range(len(shapes))]
+    res = []
+    for gg, pp in ((g, p), (gt, [x.t().contiguous() for x in p])):
+        pp = [x.clone() for x in pp]
+        b = [torch.zeros(x.shape, device="cuda") for x in gg]
+        u = [torch.empty(x.shape, device="cuda") for x in gg]
+        norms = torch.empty(len(gg), device="cuda")
+        nsa.muon_step(pp, gg, b, update_out=u, norms_out=norms)
+        torch.cuda.synchronize()
+        res.append((pp, b, u, norms))
+    (p0, b0, u0, n0), (p1, b1, u1, n1) = res
+    assert torch.equal(n0, n1)
+    for i, s in enumerate(shapes):
+        assert torch.equal(u1[i], u0[i].t()), s
+        assert torch.equal(p1[i], p0[i].t()), s
+        assert torch.equal(b1[i], b0[i].t()), s
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_more_than_sixteen_shape_groups(dtype):
+    """One call with 21 distinct padded shapes (m', n') = (256 a, 256 b), both
+    orientations, ragged: every contraction launch table holds at most 16
+    shape groups, so each product runs as two launches with their own tile
+    numbering and XCD mapping.  17 of the 18 groups with m' <= 512 have their
+    Gram cut into K slices (K = 11 * 256 has no slice count in 2..8), so split
+    segments land in both Gram launches and the slice sums need two launches
+    as well.  Every matrix against the oracle."""
+    shapes = []
+    for a, bs in ((1, range(2, 11)), (2, range(3, 12)), (3, range(4, 7))):
+        for b in bs:
+            r, c = 256 * a - 5 * a, 256 * b - 11
+            shapes.append((r, c) if (a + b) % 2 else (c, r))
+    assert len({(-(-min(s) // 256), -(-max(s) // 256)) for s in shapes}) == 21
+    cfg = _adhoc(shapes, dtype, 236 + (dtype == "bf16"))
+    print(f"[parity] 21 shape groups, {dtype}", flush=True)
+    nsa.profile_read()
+    nsa.profile_enable(True)
+    res = run_muon(cfg, ns_steps=5)
+    nsa.profile_enable(False)
+    prof = nsa.profile_read()
+    assert prof["ns_gemm"]["launches"] == 2 * 5
+    assert prof["syrk"]["launches"] == 4 * 5          # two product tables + two slice-sum tables
+    check_against_oracle(cfg, res, ns_steps=5)
+
+
+def test_side_stream_allocations_outlive_the_call():
+    """ns_batched and the one-shot muon_step allocate their workspace (and
+    ns_batched its outputs) from the current stream's pool but run on the
+    given stream.  A same-size block allocated and filled on the current
+    stream right after each call must not be one of those blocks while the
+    side stream still uses them: the results must still meet the oracle."""
+    shapes = [(2048, 6144), (6144, 2048), (2048, 6144)]
+    cfg = _adhoc(shapes, "bf16", 240, grad_scale=1e-3)
+    xs = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(len(shapes))]
+    dx = [to_device(x) for x in xs]
+    need = nsa.ns_workspace_bytes(shapes, torch.bfloat16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = nsa.ns_batched(dx, ns_steps=5, stream=side)
+    junk = torch.empty(need, dtype=torch.uint8, device="cuda")
+    junk.fill_(0xFF)
+    junk_outs = [torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda") for s in shapes]
+    side.synchronize()
+    torch.cuda.synchronize()
+    for x, o, s in zip(xs, outs, shapes):
+        assert rel_fro(to_host_f64(o), oracle.newton_schulz(x.as_f64(), 5)) <= TOL["bf16"], s
+    del junk, junk_outs
+    # the one-shot Muon step: its workspace is dropped on return
+    p0 = [to_device(gen.draw_matrix(cfg, i, gen.WEIGHT)) for i in range(len(shapes))]
+    p = [t.clone() for t in p0]
+    b = [torch.zeros(s, device="cuda") for s in shapes]
+    u = [torch.empty(s, device="cuda") for s in shapes]
+    need = nsa.muon_step_workspace_bytes(shapes, torch.bfloat16)
+    torch.cuda.synchronize()
+    nsa.muon_step(p, dx, b, update_out=u, stream=side)
+    junk = torch.empty(need, dtype=torch.uint8, device="cuda")
+    junk.fill_(0xFF)
+    side.synchronize()
+    torch.cuda.synchronize()
+    for i, s in enumerate(shapes):
+        _, _, uw, _ = oracle.muon_step([to_host_f64(p0[i])], [xs[i].as_f64()], [np.zeros(s)], f32_mu(0.95), True, 5,
+                                       0.02)
+        assert rel_fro(to_host_f64(u[i]), uw[0]) <= TOL["bf16"], s
