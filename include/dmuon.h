@@ -29,8 +29,10 @@
  * - Tensor pointers are device pointers; the pointer arrays themselves, the
  *   shape arrays and lr_scale are host arrays, read only during the call.
  * - All tensors and the workspace are owned by the caller.  The library
- *   allocates no device memory; it keeps no state between calls other than
- *   per-device capability checks and the optional profiler record.
+ *   allocates no device memory at run time; its only device memory is the
+ *   static scratch of dmuon_muon_step_noalloc, which comes with the library's
+ *   code on each GPU.  It keeps no state between calls other than per-device
+ *   capability checks, the scratch addresses and the optional profiler record.
  * - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *   and the call returns without synchronising.  Inputs must stay valid and
  *   unmodified until the stream reaches the end of the enqueued work.
@@ -194,6 +196,31 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
                     int lr_scale_mode, const float* lr_scale,
                     float* const* update_out, float* norms_out,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Scratch held by the library for dmuon_muon_step_noalloc: 64 MiB on each GPU
+ * the library is loaded on, from the load until the process ends. */
+#define DMUON_NOALLOC_SCRATCH_BYTES 67108864
+
+/*
+ * dmuon_muon_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as dmuon_muon_step (bitwise: the same kernels),
+ * but the scratch is the library's own static device array of
+ * DMUON_NOALLOC_SCRATCH_BYTES per GPU instead of a caller workspace; the call
+ * allocates nothing.  A set whose dmuon_muon_step_workspace_bytes exceeds
+ * DMUON_NOALLOC_SCRATCH_BYTES is rejected with DMUON_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams or threads) race and give undefined
+ * results; calls ordered on one stream are safe.  The array needs no clearing
+ * between calls (every stage writes what it later reads).  The stream-capture
+ * restriction of dmuon_muon_step applies as well (host-side descriptors).
+ */
+int dmuon_muon_step_noalloc(int count, void* const* params, const void* const* grads, float* const* momentum,
+                            const int64_t* rows, const int64_t* cols, int dtype,
+                            int ns_steps, const dmuon_ns_config* ns_config,
+                            float mu, int nesterov, float lr, float weight_decay,
+                            int lr_scale_mode, const float* lr_scale,
+                            float* const* update_out, float* norms_out, void* hip_stream);
 
 /*
  * Workspace size for dmuon_clip_grad_norm, in bytes.  Needs no GPU.

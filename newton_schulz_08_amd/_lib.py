@@ -27,6 +27,7 @@ DMUON_ERR_HIP = 6
 DMUON_MIN_NS_NUMEL = 100000
 DMUON_MAX_DIM = 65536
 DMUON_MAX_NS_STEPS = 64
+DMUON_NOALLOC_SCRATCH_BYTES = 67108864
 
 DMUON_NS_GRAM = 0
 DMUON_NS_DIRECT = 1
@@ -71,6 +72,9 @@ SIGNATURES = {
     "dmuon_muon_step": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _I64P, _I64P, ctypes.c_int, ctypes.c_int,
                                        _CFGP, ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_int, _FP, _PP, _P, _P, ctypes.c_size_t, _P]),
+    "dmuon_muon_step_noalloc": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _I64P, _I64P, ctypes.c_int, ctypes.c_int,
+                                               _CFGP, ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                               ctypes.c_int, _FP, _PP, _P, _P]),
     "dmuon_clip_grad_norm_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, ctypes.c_int, _SZP]),
     "dmuon_clip_grad_norm": (ctypes.c_int, [ctypes.c_int, _PP, _I64P, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                             ctypes.c_int, _FP, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),

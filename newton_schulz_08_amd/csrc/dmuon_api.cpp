@@ -844,6 +844,35 @@ int prepare_muon_step(int count, void* const* params, const void* const* grads, 
   return DMUON_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// The scratch of dmuon_muon_step_noalloc.  Each GPU the library is loaded on
+// holds its own copy until the process ends.  In host code this name is only
+// a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever used.
+static __device__ __align__(256) char scratch[DMUON_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, char*> g_scratch_ptr;   // device -> address of that device's scratch
+
+// Address of the current device's scratch, looked up on its first use.
+int scratch_for_current_device(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DMUON_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return fail(DMUON_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    }
+    it = g_scratch_ptr.emplace(dev, static_cast<char*>(ptr)).first;
+  }
+  *out = it->second;
+  return DMUON_OK;
+}
+
 }  // namespace
 }  // namespace dmuon
 
@@ -864,6 +893,29 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
   if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
   if ((st = check_device(hip_stream)) != DMUON_OK) return st;
   return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+int dmuon_muon_step_noalloc(int count, void* const* params, const void* const* grads, float* const* momentum,
+                            const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
+                            const dmuon_ns_config* ns_config, float mu, int nesterov, float lr, float weight_decay,
+                            int lr_scale_mode, const float* lr_scale, float* const* update_out, float* norms_out,
+                            void* hip_stream) {
+  g_last_error.clear();
+  Plan pl;
+  Call call{};
+  bool empty = false;
+  int st = prepare_muon_step(count, params, grads, momentum, rows, cols, dtype, ns_steps, ns_config, mu, nesterov,
+                             lr, weight_decay, lr_scale_mode, lr_scale, update_out, norms_out, &pl, &call, &empty);
+  if (st != DMUON_OK || empty) return st;
+  if (pl.total > DMUON_NOALLOC_SCRATCH_BYTES)
+    return fail(DMUON_ERR_WORKSPACE, "this call needs " + std::to_string(pl.total) +
+                                         " bytes of scratch; dmuon_muon_step_noalloc has DMUON_NOALLOC_SCRATCH_BYTES (" +
+                                         std::to_string(static_cast<size_t>(DMUON_NOALLOC_SCRATCH_BYTES)) +
+                                         "); use dmuon_muon_step with a workspace");
+  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
+  char* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != DMUON_OK) return st;
+  return run(pl, call, ws, static_cast<hipStream_t>(hip_stream));
 }
 
 int dmuon_clip_grad_norm_workspace_bytes(int count, const int64_t* numel, int num_segments, size_t* bytes_out) {
