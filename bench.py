@@ -79,7 +79,52 @@ def cpu_baseline(cfg, sample_idx, ns_steps, mu, lr):
     return {"value": (s + g) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one Muon step (k={ns_steps}) of {len(sample_idx)} matrices: {desc}; {dt:.2f} s wall, "
                       f"float64 NumPy oracle",
+            "flop_count": "algorithmic: m'(m'+1)n' + 2m'^2 n' + 3m'n' per matrix and step, the count the GPU "
+                          "figure uses (the oracle itself forms the full X X^T, the dense-equivalent count)",
+            "value_dense_equivalent": dense_equivalent_flops(shapes, ns_steps) / dt / 1e12,
+            "wall_s": dt, "per_config": cpu_baseline_small_sets(),
             "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline_small_sets():
+    """Wall time of the fp64 oracle over the two small sets in full: the
+    TinyMLP set (one Muon step, k = 5) and the spectrum set (Newton-Schulz of
+    all 32 matrices for k in {3, 5, 7, 10}, from its fp32 and its bf16 copy).
+    Input generation is not timed."""
+    import numpy as np
+    import oracle
+    from workloads import gen, get_config
+    out = {}
+    tiny = get_config("tinymlp_f32")
+    mats = [(gen.draw_matrix(tiny, i, gen.WEIGHT).as_f64(), gen.draw_matrix(tiny, i, gen.GRAD).as_f64())
+            for i in range(tiny.count)]
+    mu = float(np.float32(tiny.momentum))
+    t0 = time.perf_counter()
+    for p, g in mats:
+        oracle.muon_step([p], [g], [np.zeros_like(g)], mu, tiny.nesterov, 5, tiny.lr)
+    dt = time.perf_counter() - t0
+    shapes = [(m.rows, m.cols) for m in tiny.matrices]
+    s, gf = ns_flops(shapes, 5)
+    out["tinymlp_f32"] = {"what": f"one Muon step, k=5, all {tiny.count} matrices", "wall_s": dt,
+                          "tflops": (s + gf) / dt / 1e12,
+                          "tflops_dense_equivalent": dense_equivalent_flops(shapes, 5) / dt / 1e12}
+    spec = get_config("spectrum")
+    ins = []
+    for i, m in enumerate(spec.matrices):
+        f32, b16 = gen.spectrum_copies(gen.spectrum_matrix(spec.cfg_id, i, m.rows, m.cols)[0])
+        ins += [f32.as_f64(), b16.as_f64()]
+    t0 = time.perf_counter()
+    for k in spec.ns_steps:
+        for x in ins:
+            oracle.newton_schulz(x, k)
+    dt = time.perf_counter() - t0
+    shapes = [(m.rows, m.cols) for m in spec.matrices] * 2
+    flops = sum(sum(ns_flops(shapes, k)) for k in spec.ns_steps)
+    dense = sum(dense_equivalent_flops(shapes, k) for k in spec.ns_steps)
+    out["spectrum"] = {"what": f"Newton-Schulz of all {spec.count} matrices for k in {list(spec.ns_steps)}, "
+                               "fp32 and bf16 copies", "wall_s": dt, "tflops": flops / dt / 1e12,
+                       "tflops_dense_equivalent": dense / dt / 1e12}
+    return out
 
 
 def cpu_model():
@@ -275,6 +320,43 @@ def clip_bench(torch, nsa, grads, reps=5):
         ms = st["total_ms"] / st["launches"]
         gbs = numel * bytes_per / (ms * 1e-3) / 1e9
         out[tag] = {"ms": ms, "algorithmic_bytes": numel * bytes_per, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+    return out
+
+
+def fused_clip_bench(torch, nsa, params, grads, moms, cfg, ns_steps, plain_step_ms, reps=3):
+    """The Muon step with per-segment clipping folded in (one segment per
+    projection kind, each clipped to half its norm): the clip's partials pass
+    (timed by the library's kernel events) is its only extra work, one read of
+    the gradients; the step itself reads the gradients as before, scaled on
+    load."""
+    kinds = sorted({g.shape for g in grads})
+    segs = [kinds.index(g.shape) for g in grads]
+    totals = torch.zeros(len(kinds), device="cuda")
+    ws = nsa.alloc_workspace(nsa.clip_grad_norm_workspace_bytes([g.numel() for g in grads], len(kinds)))
+    totals = nsa.clip_grad_norm_(grads, [3.0e38] * len(kinds), segs, workspace=ws)   # totals only: nothing clips
+    max_norm = [0.5 * float(t) for t in totals.cpu()]
+    del ws
+    step = nsa.MuonStep(params, grads, moms, ns_steps=ns_steps, mu=cfg.momentum, nesterov=cfg.nesterov, lr=cfg.lr,
+                        clip_max_norm=max_norm, clip_segments=segs)
+    step()
+    torch.cuda.synchronize()
+    nsa.profile_read()
+    nsa.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    nsa.profile_enable(False)
+    st = nsa.profile_read().get("grad_clip")
+    numel = sum(g.numel() for g in grads)
+    clip_ms = st["total_ms"] / st["launches"]
+    out = {"step_ms": ms, "plain_step_ms": plain_step_ms, "clip_ms": clip_ms,
+           "clip_algorithmic_bytes": numel * grads[0].element_size(),
+           "clip_gbs": numel * grads[0].element_size() / (clip_ms * 1e-3) / 1e9,
+           "segments": len(kinds), "max_norm": "half of each segment's norm"}
+    del step
+    torch.cuda.empty_cache()
     return out
 
 
@@ -506,8 +588,12 @@ def main():
         "meta": {**metadata(torch), **static_info, "timed_region_clocks": clocks},
     }
     if not args.no_clip_bench:
-        # after the timed steps: the clipping pass rescales the gradients in place
+        del step
+        torch.cuda.empty_cache()
+        # before the in-place clipping pass below, which rescales the gradients
+        fused = fused_clip_bench(torch, nsa, params, grads, moms, cfg, ns_steps, ms_per_step)
         out["grad_clip"] = clip_bench(torch, nsa, grads)
+        out["grad_clip"]["fused_in_step"] = fused
     if not args.no_adamw_bench:
         out["adamw"] = adamw_bench(torch, nsa, torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)
     if not args.no_reference_gemm and cfg.dtype == "bf16":

@@ -197,6 +197,45 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
                     float* const* update_out, float* norms_out,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Workspace size for dmuon_muon_step_clipped, in bytes: that of
+ * dmuon_muon_step for the same shapes and configuration, plus the clip's
+ * per-tile partial sums and per-segment coefficients.  Needs no GPU.
+ */
+int dmuon_muon_step_clip_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                                         const dmuon_ns_config* ns_config, int num_segments, size_t* bytes_out);
+
+/*
+ * dmuon_muon_step with per-segment global p-norm gradient clipping folded in
+ * (training guide, "梯度裁剪": the Muon clip runs on the reduced gradients
+ * before momentum and Newton-Schulz; "regular / Muon / AdamW 的融合 CUDA 裁剪":
+ * per-segment norms and coefficients computed in one fused pass).  The clip is
+ * dmuon_clip_grad_norm's rule with the matrices as its tensors:
+ *
+ *   total_s = || gradients of segment s ||_p
+ *   coef_s  = min(max_norm[s] / (total_s + 1e-6), 1)
+ *
+ * and the step then runs on coef_{segment[i]} * grads[i], formed in fp32 as
+ * each gradient element is read and never rounded to the gradient dtype.  The
+ * caller's gradients are not rewritten (unlike dmuon_clip_grad_norm), which
+ * saves that pass: clipping costs one extra read of the gradients.
+ *
+ * segment[i]   : host, the clipping segment of matrix i, in [0, num_segments).
+ * num_segments, max_norm (host, finite, >= 0), norm_type (p > 0 or +inf),
+ * totals_out (NULL or device float32[num_segments]): as in
+ * dmuon_clip_grad_norm.  Every other argument as in dmuon_muon_step; the
+ * workspace is sized by dmuon_muon_step_clip_workspace_bytes.  A segment whose
+ * coefficient is 1 gets bitwise the result of dmuon_muon_step.
+ */
+int dmuon_muon_step_clipped(int count, void* const* params, const void* const* grads, float* const* momentum,
+                            const int64_t* rows, const int64_t* cols, int dtype,
+                            int ns_steps, const dmuon_ns_config* ns_config,
+                            float mu, int nesterov, float lr, float weight_decay,
+                            int lr_scale_mode, const float* lr_scale,
+                            float* const* update_out, float* norms_out,
+                            const int* segment, int num_segments, const float* max_norm, float norm_type,
+                            float* totals_out, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Scratch held by the library for dmuon_muon_step_noalloc: 64 MiB on each GPU
  * the library is loaded on, from the load until the process ends. */
 #define DMUON_NOALLOC_SCRATCH_BYTES 67108864
@@ -290,6 +329,22 @@ int dmuon_adamw_step(int count, void* const* params, const void* const* grads, f
                      float* const* exp_avg_sq, const int64_t* numel, int dtype, int step, float lr, float beta1,
                      float beta2, float eps, float weight_decay, void* workspace, size_t workspace_bytes,
                      void* hip_stream);
+
+/*
+ * The plan of a call as text: routes (numel < DMUON_MIN_NS_NUMEL goes
+ * elementwise when muon_step is nonzero), shape groups with their transposed
+ * count, tiles and K slices, launches per Newton-Schulz step, algorithmic
+ * flops and the workspace size -- the analogue of the training guide's INFO
+ * summary of how parameters were assigned ("日志与调试", "验证参数分配").
+ * Writes at most buf_len bytes including the terminating NUL (buf may be NULL
+ * when buf_len is 0) and sets *needed (if not NULL) to the full length + 1.
+ * Needs no GPU.  With the environment variable DMUON_LOG set (to anything but
+ * "" or "0"), every call prints this text to stderr when its plan differs from
+ * the last one printed.
+ */
+int dmuon_plan_summary(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                       const dmuon_ns_config* ns_config, int ns_steps, int muon_step, char* buf, size_t buf_len,
+                       size_t* needed);
 
 /* Static text for a status code.  The codes translate the pages' error
  * conventions to return values: the blog's newton_schulz asserts a 2-D input

@@ -11,11 +11,13 @@ from .api import (  # noqa: F401
     adamw_step_workspace_bytes,
     alloc_workspace,
     backend_info,
+    plan_summary,
     clip_grad_norm_,
     clip_grad_norm_workspace_bytes,
     dtype_code,
     muon_step,
     muon_step_workspace_bytes,
+    muon_step_clip_workspace_bytes,
     ns_batched,
     ns_config,
     ns_workspace_bytes,

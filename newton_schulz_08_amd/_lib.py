@@ -72,6 +72,12 @@ SIGNATURES = {
     "dmuon_muon_step": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _I64P, _I64P, ctypes.c_int, ctypes.c_int,
                                        _CFGP, ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_int, _FP, _PP, _P, _P, ctypes.c_size_t, _P]),
+    "dmuon_muon_step_clip_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64P, _I64P, ctypes.c_int, _CFGP,
+                                                            ctypes.c_int, _SZP]),
+    "dmuon_muon_step_clipped": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _I64P, _I64P, ctypes.c_int, ctypes.c_int,
+                                               _CFGP, ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                               ctypes.c_int, _FP, _PP, _P, ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                               _FP, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
     "dmuon_muon_step_noalloc": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _I64P, _I64P, ctypes.c_int, ctypes.c_int,
                                                _CFGP, ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                                ctypes.c_int, _FP, _PP, _P, _P]),
@@ -82,6 +88,8 @@ SIGNATURES = {
     "dmuon_adamw_step": (ctypes.c_int, [ctypes.c_int, _PP, _PP, _PP, _PP, _I64P, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                         ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "dmuon_plan_summary": (ctypes.c_int, [ctypes.c_int, _I64P, _I64P, ctypes.c_int, _CFGP, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_char_p, ctypes.c_size_t, _SZP]),
     "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dmuon_last_error": (ctypes.c_char_p, []),
     "dmuon_backend_info": (ctypes.c_char_p, []),

@@ -115,6 +115,17 @@ def muon_step_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtyp
     return int(out.value)
 
 
+def muon_step_clip_workspace_bytes(shapes: Sequence[Sequence[int]], dtype: torch.dtype, num_segments: int = 1,
+                                   ns_coeffs=None, ns_backend: str = "gram") -> int:
+    rows, cols = _shape_arrays(shapes)
+    out = ctypes.c_size_t(0)
+    cfg = ns_config(ns_coeffs, ns_backend)
+    check(_lib.load().dmuon_muon_step_clip_workspace_bytes(len(shapes), rows, cols, dtype_code(dtype), _cfg_ptr(cfg),
+                                                           int(num_segments), ctypes.byref(out)),
+          "dmuon_muon_step_clip_workspace_bytes")
+    return int(out.value)
+
+
 def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
     """A uint8 device buffer of at least nbytes, 256-byte aligned."""
     ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
@@ -187,7 +198,9 @@ class MuonStep:
                  lr: float = 0.02, lr_scale: Optional[Sequence[float]] = None, weight_decay: float = 0.0,
                  lr_scale_mode: str = "one", ns_coeffs=None, ns_backend: str = "gram",
                  update_out: Optional[Sequence[Optional[torch.Tensor]]] = None,
-                 norms_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                 norms_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 clip_max_norm=None, clip_segments: Optional[Sequence[int]] = None, clip_norm_type: float = 2.0,
+                 clip_totals: Optional[torch.Tensor] = None):
         n = len(params)
         if not (len(grads) == len(momentum) == n):
             raise ValueError("params, grads and momentum must have the same length")
@@ -229,7 +242,26 @@ class MuonStep:
             raise ValueError(f"lr_scale_mode must be 'one' or 'moonlight', got {lr_scale_mode!r}")
         self._scale_mode = modes[lr_scale_mode]
         self._cfg = ns_config(ns_coeffs, ns_backend, self.ns_steps)
-        self.workspace_bytes = muon_step_workspace_bytes(self.shapes, dt, ns_coeffs, ns_backend)
+        # optional clipping folded into the step (dmuon_muon_step_clipped): one
+        # max norm per segment, a segment index per matrix (default all 0)
+        self.clip = clip_max_norm is not None
+        if self.clip:
+            mn = [float(clip_max_norm)] if not hasattr(clip_max_norm, "__len__") else [float(v) for v in clip_max_norm]
+            seg = [0] * n if clip_segments is None else [int(v) for v in clip_segments]
+            if len(seg) != n:
+                raise ValueError("clip_segments must have one entry per matrix")
+            if clip_totals is not None and (clip_totals.dtype != torch.float32 or not clip_totals.is_cuda or
+                                            clip_totals.numel() < len(mn)):
+                raise ValueError("clip_totals must be a float32 device tensor with one entry per segment")
+            self._clip_nseg = len(mn)
+            self._clip_max = (ctypes.c_float * len(mn))(*mn)
+            self._clip_seg = (ctypes.c_int * n)(*seg)
+            self._clip_p = float(clip_norm_type)
+            self._clip_totals = ctypes.c_void_p(clip_totals.data_ptr()) if clip_totals is not None else None
+            self._keep = self._keep + (clip_totals,)
+            self.workspace_bytes = muon_step_clip_workspace_bytes(self.shapes, dt, len(mn), ns_coeffs, ns_backend)
+        else:
+            self.workspace_bytes = muon_step_workspace_bytes(self.shapes, dt, ns_coeffs, ns_backend)
         self._own_ws = workspace is None
         self.workspace = workspace if workspace is not None else alloc_workspace(self.workspace_bytes,
                                                                                  params[0].device)
@@ -238,12 +270,18 @@ class MuonStep:
         self._lib = _lib.load()
 
     def __call__(self, stream=None) -> None:
-        check(self._lib.dmuon_muon_step(
-            self.count, self._params, self._grads, self._mom, self._rows, self._cols, dtype_code(self.dtype),
-            self.ns_steps, _cfg_ptr(self._cfg), ctypes.c_float(self.mu), 1 if self.nesterov else 0,
-            ctypes.c_float(self.lr), ctypes.c_float(self.weight_decay), self._scale_mode,
-            self._scale, self._upd, self._norms, ctypes.c_void_p(self.workspace.data_ptr()),
-            self.workspace.numel(), ctypes.c_void_p(_stream_handle(stream))), "dmuon_muon_step")
+        common = (self.count, self._params, self._grads, self._mom, self._rows, self._cols, dtype_code(self.dtype),
+                  self.ns_steps, _cfg_ptr(self._cfg), ctypes.c_float(self.mu), 1 if self.nesterov else 0,
+                  ctypes.c_float(self.lr), ctypes.c_float(self.weight_decay), self._scale_mode,
+                  self._scale, self._upd, self._norms)
+        tail = (ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                ctypes.c_void_p(_stream_handle(stream)))
+        if self.clip:
+            check(self._lib.dmuon_muon_step_clipped(*common, self._clip_seg, self._clip_nseg, self._clip_max,
+                                                    ctypes.c_float(self._clip_p), self._clip_totals, *tail),
+                  "dmuon_muon_step_clipped")
+        else:
+            check(self._lib.dmuon_muon_step(*common, *tail), "dmuon_muon_step")
         if self._own_ws:
             _used_on(stream, self.workspace)
 
@@ -362,6 +400,22 @@ class AdamWStep:
         adamw_step_(self.params, self.grads, self.exp_avg, self.exp_avg_sq, self.step, self.lr, self.betas,
                     self.eps, self.weight_decay, self.workspace, stream)
         _used_on(stream, self.workspace, *self.exp_avg, *self.exp_avg_sq)
+
+
+def plan_summary(shapes: Sequence[Sequence[int]], dtype: torch.dtype, ns_steps: int = 5, muon: bool = True,
+                 ns_coeffs=None, ns_backend: str = "gram") -> str:
+    """dmuon_plan_summary: how a call over these shapes is routed, grouped and
+    launched, as text (no GPU needed)."""
+    rows, cols = _shape_arrays(shapes)
+    cfg = ns_config(ns_coeffs, ns_backend, int(ns_steps))
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    check(lib.dmuon_plan_summary(len(shapes), rows, cols, dtype_code(dtype), _cfg_ptr(cfg), int(ns_steps),
+                                 1 if muon else 0, None, 0, ctypes.byref(need)), "dmuon_plan_summary")
+    buf = ctypes.create_string_buffer(need.value)
+    check(lib.dmuon_plan_summary(len(shapes), rows, cols, dtype_code(dtype), _cfg_ptr(cfg), int(ns_steps),
+                                 1 if muon else 0, buf, need.value, None), "dmuon_plan_summary")
+    return buf.value.decode()
 
 
 def backend_info() -> str:

@@ -23,9 +23,11 @@ struct alignas(16) ClipDesc {
 };
 static_assert(sizeof(ClipDesc) == 32, "ClipDesc layout");
 
-// partials (one per tile) -> per-segment totals and coefficients -> in-place scale.
+// partials (one per tile) -> per-segment totals and coefficients -> in-place
+// scale (scale != 0; otherwise the coefficients are left for a consumer that
+// applies them on load, as the Muon step's prologue does).
 hipError_t launch_clip(int dt, const ClipDesc* descs, const int* tile_prefix, int n, int total_tiles,
                        const int* seg_tile0, int nseg, const float* max_norm, int kind, float p, float* partials,
-                       float* coefs, float* totals_out, int grid, hipStream_t stream);
+                       float* coefs, float* totals_out, int scale, int grid, hipStream_t stream);
 
 }  // namespace dmuon

@@ -65,7 +65,7 @@ struct alignas(16) MatDesc {
   int ew_cols;       // covered extent (cols) for the prologue
   int vec_ok;        // 1 when 4-element vector access is aligned for g/buf/p/upd
   float lr_scale;
-  float pad_;
+  int clip_seg;      // clipping segment of the gradient (its coefficient scales g on load)
 };
 static_assert(sizeof(MatDesc) == 128, "MatDesc layout");
 

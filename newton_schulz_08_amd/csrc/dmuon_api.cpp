@@ -373,6 +373,8 @@ struct Call {
   float decay;               // 1 - lr * weight_decay
   int nesterov;
   NsCfg ns;
+  const float* gcoef = nullptr;   // device, per-segment clipping coefficients (NULL: no clipping)
+  const int* clip_seg = nullptr;  // host, per matrix: its clipping segment
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -421,6 +423,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     // training guide, "超参数指南", lr row: 0.2 * sqrt(max(m, n)) per parameter
     if (call.moonlight) s *= static_cast<float>(0.2 * std::sqrt(static_cast<double>(std::max(mp.m, mp.n))));
     d.lr_scale = s;
+    d.clip_seg = call.clip_seg ? call.clip_seg[i] : 0;
     prefix[k] = tile0;
     tile0 += mp.ew_tiles;
   }
@@ -451,7 +454,7 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
   const int ew_grid = std::min(pl.total_tiles, 1 << 22);   // one block per tile
   hipError_t e = timed(kKPrologue, 0.0, pro_bytes, stream, [&] {
     return launch_prologue(dt, d_descs, d_prefix, pl.count, pl.total_tiles, d_partials, call.mode, call.mu,
-                           call.nesterov, call.lr, call.decay, ew_grid, stream);
+                           call.nesterov, call.lr, call.decay, call.gcoef, ew_grid, stream);
   });
   if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("prologue launch: ") + hipGetErrorString(e));
   e = timed(kKNorm, 0.0, 16.0 * pl.total_tiles, stream, [&] {
@@ -673,6 +676,68 @@ ClipPlan make_clip_plan(int count, const int64_t* numel, const int* segment, int
   return cp;
 }
 
+// Clip arguments shared by dmuon_clip_grad_norm and dmuon_muon_step_clipped
+// (counts and numel are checked by validate_clip).
+int validate_clip_args(int count, const int* segment, int nseg, const float* max_norm, float norm_type) {
+  if (!(norm_type > 0.0f)) return fail(DMUON_ERR_INVALID_ARG, "norm_type must be > 0 (or +inf)");
+  if (!max_norm) return fail(DMUON_ERR_INVALID_ARG, "max_norm array is NULL");
+  for (int s = 0; s < nseg; ++s)
+    if (!std::isfinite(max_norm[s]) || max_norm[s] < 0.0f)
+      return fail(DMUON_ERR_INVALID_ARG, "max_norm entries must be finite and >= 0");
+  if (count > 0 && !segment) return fail(DMUON_ERR_INVALID_ARG, "segment array is NULL");
+  for (int i = 0; i < count; ++i)
+    if (segment[i] < 0 || segment[i] >= nseg)
+      return fail(DMUON_ERR_INVALID_ARG, "segment[" + std::to_string(i) + "] outside [0, num_segments)");
+  return DMUON_OK;
+}
+
+// Enqueues the clip over the plan `cp` (laid out at ws): partials, per-segment
+// totals and coefficients, and with `scale` the in-place rewrite.  Returns the
+// device address of the coefficients through *coefs.
+int enqueue_clip(const ClipPlan& cp, int count, const void* const* grads, const int64_t* numel, int dtype,
+                 const int* segment, int nseg, const float* max_norm, float norm_type, float* totals_out, char* ws,
+                 int scale, hipStream_t stream, float** coefs) {
+  std::vector<ClipDesc> descs(std::max(count, 1));
+  double bytes = 0.0;
+  for (int k = 0; k < count; ++k) {
+    const int i = cp.order[k];
+    ClipDesc& d = descs[k];
+    std::memset(&d, 0, sizeof(d));
+    d.g = const_cast<void*>(grads[i]);
+    d.numel = numel[i];
+    d.segment = segment[i];
+    d.vec_ok = aligned(grads[i], 16) ? 1 : 0;
+    bytes += static_cast<double>(numel[i]) * elem_bytes(dtype);
+  }
+  ClipDesc* d_descs = reinterpret_cast<ClipDesc*>(ws + cp.off_descs);
+  int* d_prefix = reinterpret_cast<int*>(ws + cp.off_prefix);
+  int* d_seg = reinterpret_cast<int*>(ws + cp.off_seg);
+  float* d_maxn = reinterpret_cast<float*>(ws + cp.off_maxn);
+  float* d_coef = reinterpret_cast<float*>(ws + cp.off_coef);
+  float* d_part = reinterpret_cast<float*>(ws + cp.off_part);
+  if (hipMemcpyAsync(d_descs, descs.data(), sizeof(ClipDesc) * count, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(d_prefix, cp.tile_prefix.data(), sizeof(int) * (count + 1), hipMemcpyHostToDevice, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(d_seg, cp.seg_tile0.data(), sizeof(int) * (nseg + 1), hipMemcpyHostToDevice, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(d_maxn, max_norm, sizeof(float) * nseg, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return fail(DMUON_ERR_HIP, std::string("clip descriptor upload failed: ") + hipGetErrorString(hipGetLastError()));
+  const int kind = std::isinf(norm_type) ? kClipPInf
+                   : norm_type == 2.0f    ? kClipP2
+                   : norm_type == 1.0f    ? kClipP1
+                                          : kClipPGeneral;
+  const int tiles = cp.tile_prefix[count];
+  const int grid = std::max(1, std::min(tiles, 1 << 22));   // one block per tile
+  // algorithmic bytes: one read, plus a read and a write when rewriting (counted as read only here)
+  hipError_t e = timed(kKClip, 0.0, bytes, stream, [&] {
+    return launch_clip(dtype, d_descs, d_prefix, count, tiles, d_seg, nseg, d_maxn, kind, norm_type, d_part, d_coef,
+                       totals_out, scale, grid, stream);
+  });
+  if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("clip launch: ") + hipGetErrorString(e));
+  if (coefs) *coefs = d_coef;
+  return DMUON_OK;
+}
+
 // ---------------------------------------------------------------- AdamW
 struct AdamPlan {
   std::vector<int> tile_prefix;  // size n + 1
@@ -707,6 +772,67 @@ AdamPlan make_adamw_plan(int count, const int64_t* numel) {
   off = align_up(off + sizeof(int) * (count + 1));
   ap.total = off;
   return ap;
+}
+
+// Human-readable plan: routes, shape groups, tiles, launches and algorithmic
+// flops (the analogue of the training guide's INFO summary of how parameters
+// were assigned, "日志与调试").
+std::string plan_summary(const Plan& pl, const NsCfg& ns, int ns_steps, bool muon) {
+  auto fmt = [](const char* f, auto... a) {
+    char b[256];
+    std::snprintf(b, sizeof(b), f, a...);
+    return std::string(b);
+  };
+  int tall = 0;
+  for (int k = 0; k < pl.n_ns; ++k) tall += pl.mats[k].tr ? 1 : 0;
+  std::string s = fmt("dmuon plan: %s over %d matrices (%s), ns_steps %d: %d Newton-Schulz in %zu shape groups "
+                      "(%d iterated on the transpose), %d elementwise (numel < %d)\n",
+                      muon ? "muon_step" : "ns_batched", pl.count, pl.dt == kBF16 ? "bf16" : "fp32", ns_steps,
+                      pl.n_ns, pl.groups.size(), tall, pl.count - pl.n_ns, DMUON_MIN_NS_NUMEL);
+  int split = 0;
+  for (size_t i = 0; i < pl.groups.size(); ++i) {
+    const Group& g = pl.groups[i];
+    const int64_t T = g.mp / kTile, TN = g.np / kTile;
+    double fl = 0.0;
+    int gt = 0;
+    for (int k = g.first; k < g.first + g.count; ++k) {
+      const double mm = static_cast<double>(std::min(pl.mats[k].m, pl.mats[k].n));
+      const double nn = static_cast<double>(std::max(pl.mats[k].m, pl.mats[k].n));
+      fl += mm * (mm + 1.0) * nn + 2.0 * mm * mm * nn + 3.0 * mm * nn;
+      gt += pl.mats[k].tr ? 1 : 0;
+    }
+    if (g.ks_gram > 1) ++split;
+    s += fmt("  group %zu: %d x padded %lld x %lld (%d transposed); Gram %lld %s tiles each, K %lld%s; "
+             "update %lld tiles each; %.4g flop per NS step\n",
+             i, g.count, static_cast<long long>(g.mp), static_cast<long long>(g.np), gt,
+             static_cast<long long>(ns.direct ? T * T : T * (T + 1) / 2), ns.direct ? "full" : "lower-triangle",
+             static_cast<long long>(g.np), g.ks_gram > 1 ? fmt(" in %d slices", g.ks_gram).c_str() : "",
+             static_cast<long long>(T * TN), fl);
+  }
+  const size_t ng = pl.groups.size();
+  const size_t per = static_cast<size_t>(kMaxSegPerLaunch);
+  s += fmt("  per NS step: %zu Gram launch(es) + %zu slice-sum launch(es)%s, %zu update launch(es); "
+           "%.4g flop algorithmic (Gram %.4g, update %.4g)\n",
+           (ng + per - 1) / per, (split + per - 1) / per, ns.terms == 3 ? " + the square launches" : "",
+           (ng + per - 1) / per, pl.syrk_flops + pl.gemm_flops, pl.syrk_flops, pl.gemm_flops);
+  s += fmt("  prologue: %d tiles; workspace %zu bytes (%.2f GiB)\n", pl.total_tiles, pl.total,
+           static_cast<double>(pl.total) / (1 << 30));
+  return s;
+}
+
+// DMUON_LOG set (and not "0"): print the plan to stderr when it differs from
+// the last one printed, so a training loop logs it once.
+std::mutex g_log_mu;
+std::string g_last_logged;
+void maybe_log(const Plan& pl, const NsCfg& ns, int ns_steps, bool muon) {
+  const char* env = std::getenv("DMUON_LOG");
+  if (env == nullptr || env[0] == '\0' || std::strcmp(env, "0") == 0) return;
+  const std::string s = plan_summary(pl, ns, ns_steps, muon);
+  std::lock_guard<std::mutex> lk(g_log_mu);
+  if (s == g_last_logged) return;
+  g_last_logged = s;
+  std::fputs(s.c_str(), stderr);
+  std::fflush(stderr);
 }
 
 int ws_check(const Plan& pl, void* workspace, size_t bytes) {
@@ -769,6 +895,7 @@ int dmuon_ns_batched(int count, const void* const* x_in, void* const* x_out, con
   const Plan pl = make_plan(count, rows, cols, dtype, false, ns.terms == 3);
   if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
   if ((st = check_device(hip_stream)) != DMUON_OK) return st;
+  maybe_log(pl, ns, ns_steps, false);
   Call call{};
   call.mode = kModeNsOnly;
   call.in = x_in;
@@ -892,6 +1019,7 @@ int dmuon_muon_step(int count, void* const* params, const void* const* grads, fl
   if (st != DMUON_OK || empty) return st;
   if ((st = ws_check(pl, workspace, workspace_bytes)) != DMUON_OK) return st;
   if ((st = check_device(hip_stream)) != DMUON_OK) return st;
+  maybe_log(pl, call.ns, ns_steps, true);
   return run(pl, call, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
@@ -915,6 +1043,7 @@ int dmuon_muon_step_noalloc(int count, void* const* params, const void* const* g
   if ((st = check_device(hip_stream)) != DMUON_OK) return st;
   char* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != DMUON_OK) return st;
+  maybe_log(pl, call.ns, ns_steps, true);
   return run(pl, call, ws, static_cast<hipStream_t>(hip_stream));
 }
 
@@ -935,18 +1064,11 @@ int dmuon_clip_grad_norm(int count, void* const* grads, const int64_t* numel, in
   if (st != DMUON_OK) return st;
   if (dtype != kF32 && dtype != kBF16)
     return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "dtype must be DMUON_F32 or DMUON_BF16");
-  if (!(norm_type > 0.0f)) return fail(DMUON_ERR_INVALID_ARG, "norm_type must be > 0 (or +inf)");
-  if (!max_norm) return fail(DMUON_ERR_INVALID_ARG, "max_norm array is NULL");
-  for (int s = 0; s < num_segments; ++s)
-    if (!std::isfinite(max_norm[s]) || max_norm[s] < 0.0f)
-      return fail(DMUON_ERR_INVALID_ARG, "max_norm entries must be finite and >= 0");
+  if ((st = validate_clip_args(count, segment, num_segments, max_norm, norm_type)) != DMUON_OK) return st;
   if (count == 0) return DMUON_OK;
-  if (!segment) return fail(DMUON_ERR_INVALID_ARG, "segment array is NULL");
   if (!grads) return fail(DMUON_ERR_INVALID_ARG, "grads array is NULL");
   std::vector<std::pair<const void*, std::string>> ptrs;
   for (int i = 0; i < count; ++i) {
-    if (segment[i] < 0 || segment[i] >= num_segments)
-      return fail(DMUON_ERR_INVALID_ARG, "segment[" + std::to_string(i) + "] outside [0, num_segments)");
     if (numel[i] > 0 && !grads[i]) return fail(DMUON_ERR_INVALID_ARG, "grads[" + std::to_string(i) + "] is NULL");
     if (numel[i] > 0) ptrs.push_back({grads[i], "grads[" + std::to_string(i) + "]"});
   }
@@ -958,46 +1080,72 @@ int dmuon_clip_grad_norm(int count, void* const* grads, const int64_t* numel, in
                                          std::to_string(cp.total));
   if (!aligned(workspace, kAlign)) return fail(DMUON_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if ((st = check_device(hip_stream)) != DMUON_OK) return st;
+  return enqueue_clip(cp, count, reinterpret_cast<const void* const*>(grads), numel, dtype, segment, num_segments,
+                      max_norm, norm_type, totals_out, static_cast<char*>(workspace), 1,
+                      static_cast<hipStream_t>(hip_stream), nullptr);
+}
 
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  char* ws = static_cast<char*>(workspace);
-  std::vector<ClipDesc> descs(count);
-  double bytes = 0.0;
-  for (int k = 0; k < count; ++k) {
-    const int i = cp.order[k];
-    ClipDesc& d = descs[k];
-    std::memset(&d, 0, sizeof(d));
-    d.g = grads[i];
-    d.numel = numel[i];
-    d.segment = segment[i];
-    d.vec_ok = aligned(grads[i], 16) ? 1 : 0;
-    bytes += static_cast<double>(numel[i]) * elem_bytes(dtype);
+// Numel of each matrix, for the clip plan of a Muon step.
+std::vector<int64_t> matrix_numel(int count, const int64_t* rows, const int64_t* cols) {
+  std::vector<int64_t> v(std::max(count, 1), 0);
+  for (int i = 0; i < count; ++i) v[i] = rows[i] * cols[i];
+  return v;
+}
+
+int dmuon_muon_step_clip_workspace_bytes(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                                         const dmuon_ns_config* ns_config, int num_segments, size_t* bytes_out) {
+  g_last_error.clear();
+  if (!bytes_out) return fail(DMUON_ERR_INVALID_ARG, "bytes_out is NULL");
+  int st = validate_shapes(count, rows, cols, dtype);
+  if (st != DMUON_OK) return st;
+  if (num_segments < 1) return fail(DMUON_ERR_INVALID_ARG, "num_segments must be >= 1");
+  NsCfg ns;
+  if ((st = resolve_ns_config(ns_config, 0, false, &ns)) != DMUON_OK) return st;
+  if (count == 0) {
+    *bytes_out = 0;
+    return DMUON_OK;
   }
-  ClipDesc* d_descs = reinterpret_cast<ClipDesc*>(ws + cp.off_descs);
-  int* d_prefix = reinterpret_cast<int*>(ws + cp.off_prefix);
-  int* d_seg = reinterpret_cast<int*>(ws + cp.off_seg);
-  float* d_maxn = reinterpret_cast<float*>(ws + cp.off_maxn);
-  float* d_coef = reinterpret_cast<float*>(ws + cp.off_coef);
-  float* d_part = reinterpret_cast<float*>(ws + cp.off_part);
-  if (hipMemcpyAsync(d_descs, descs.data(), sizeof(ClipDesc) * count, hipMemcpyHostToDevice, stream) != hipSuccess ||
-      hipMemcpyAsync(d_prefix, cp.tile_prefix.data(), sizeof(int) * (count + 1), hipMemcpyHostToDevice, stream) !=
-          hipSuccess ||
-      hipMemcpyAsync(d_seg, cp.seg_tile0.data(), sizeof(int) * (num_segments + 1), hipMemcpyHostToDevice, stream) !=
-          hipSuccess ||
-      hipMemcpyAsync(d_maxn, max_norm, sizeof(float) * num_segments, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return fail(DMUON_ERR_HIP, std::string("clip descriptor upload failed: ") + hipGetErrorString(hipGetLastError()));
-  const int kind = std::isinf(norm_type) ? kClipPInf
-                   : norm_type == 2.0f    ? kClipP2
-                   : norm_type == 1.0f    ? kClipP1
-                                          : kClipPGeneral;
-  const int tiles = cp.tile_prefix[count];
-  const int grid = std::max(1, std::min(tiles, 1 << 22));   // one block per tile
-  hipError_t e = timed(kKClip, 0.0, bytes, stream, [&] {
-    return launch_clip(dtype, d_descs, d_prefix, count, tiles, d_seg, num_segments, d_maxn, kind, norm_type, d_part,
-                       d_coef, totals_out, grid, stream);
-  });
-  if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("clip launch: ") + hipGetErrorString(e));
+  const std::vector<int64_t> numel = matrix_numel(count, rows, cols);
+  *bytes_out = align_up(make_plan(count, rows, cols, dtype, true, ns.terms == 3).total) +
+               make_clip_plan(count, numel.data(), nullptr, num_segments).total;
   return DMUON_OK;
+}
+
+int dmuon_muon_step_clipped(int count, void* const* params, const void* const* grads, float* const* momentum,
+                            const int64_t* rows, const int64_t* cols, int dtype, int ns_steps,
+                            const dmuon_ns_config* ns_config, float mu, int nesterov, float lr, float weight_decay,
+                            int lr_scale_mode, const float* lr_scale, float* const* update_out, float* norms_out,
+                            const int* segment, int num_segments, const float* max_norm, float norm_type,
+                            float* totals_out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_last_error.clear();
+  Plan pl;
+  Call call{};
+  bool empty = false;
+  int st = prepare_muon_step(count, params, grads, momentum, rows, cols, dtype, ns_steps, ns_config, mu, nesterov,
+                             lr, weight_decay, lr_scale_mode, lr_scale, update_out, norms_out, &pl, &call, &empty);
+  if (st != DMUON_OK) return st;
+  if (num_segments < 1) return fail(DMUON_ERR_INVALID_ARG, "num_segments must be >= 1");
+  if ((st = validate_clip_args(count, segment, num_segments, max_norm, norm_type)) != DMUON_OK) return st;
+  if (empty) return DMUON_OK;
+  const std::vector<int64_t> numel = matrix_numel(count, rows, cols);
+  if ((st = validate_clip(count, numel.data(), num_segments)) != DMUON_OK) return st;
+  const ClipPlan cp = make_clip_plan(count, numel.data(), segment, num_segments);
+  const size_t off_clip = align_up(pl.total);
+  if (!workspace) return fail(DMUON_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < off_clip + cp.total)
+    return fail(DMUON_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                         std::to_string(off_clip + cp.total));
+  if (!aligned(workspace, kAlign)) return fail(DMUON_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((st = check_device(hip_stream)) != DMUON_OK) return st;
+  maybe_log(pl, call.ns, ns_steps, true);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  float* coefs = nullptr;
+  if ((st = enqueue_clip(cp, count, grads, numel.data(), dtype, segment, num_segments, max_norm, norm_type,
+                         totals_out, static_cast<char*>(workspace) + off_clip, 0, stream, &coefs)) != DMUON_OK)
+    return st;
+  call.gcoef = coefs;
+  call.clip_seg = segment;
+  return run(pl, call, workspace, stream);
 }
 
 int dmuon_adamw_step_workspace_bytes(int count, const int64_t* numel, size_t* bytes_out) {
@@ -1090,6 +1238,28 @@ int dmuon_adamw_step(int count, void* const* params, const void* const* grads, f
     return launch_adamw(dtype, d_descs, d_prefix, count, tiles, a, grid, stream);
   });
   if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("AdamW launch: ") + hipGetErrorString(e));
+  return DMUON_OK;
+}
+
+int dmuon_plan_summary(int count, const int64_t* rows, const int64_t* cols, int dtype,
+                       const dmuon_ns_config* ns_config, int ns_steps, int muon_step, char* buf, size_t buf_len,
+                       size_t* needed) {
+  g_last_error.clear();
+  int st = validate_shapes(count, rows, cols, dtype);
+  if (st != DMUON_OK) return st;
+  if (ns_steps < 0 || ns_steps > DMUON_MAX_NS_STEPS)
+    return fail(DMUON_ERR_INVALID_ARG, "ns_steps outside [0, DMUON_MAX_NS_STEPS]");
+  NsCfg ns;
+  if ((st = resolve_ns_config(ns_config, ns_steps, false, &ns)) != DMUON_OK) return st;
+  if (buf_len > 0 && !buf) return fail(DMUON_ERR_INVALID_ARG, "buf is NULL");
+  const std::string s =
+      plan_summary(make_plan(count, rows, cols, dtype, muon_step != 0, ns.terms == 3), ns, ns_steps, muon_step != 0);
+  if (needed) *needed = s.size() + 1;
+  if (buf_len > 0) {
+    const size_t n = std::min(s.size(), buf_len - 1);
+    std::memcpy(buf, s.data(), n);
+    buf[n] = '\0';
+  }
   return DMUON_OK;
 }
 

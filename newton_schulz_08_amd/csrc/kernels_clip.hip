@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kClipThreads) void clip_scale_kernel(const ClipDesc
 
 hipError_t launch_clip(int dt, const ClipDesc* descs, const int* tile_prefix, int n, int total_tiles,
                        const int* seg_tile0, int nseg, const float* max_norm, int kind, float p, float* partials,
-                       float* coefs, float* totals_out, int grid, hipStream_t stream) {
+                       float* coefs, float* totals_out, int scale, int grid, hipStream_t stream) {
   if (total_tiles > 0) {
     auto partials_launch = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3(grid), dim3(kClipThreads), 0, stream, descs, tile_prefix, n, total_tiles,
@@ -231,7 +231,7 @@ hipError_t launch_clip(int dt, const ClipDesc* descs, const int* tile_prefix, in
   hipLaunchKernelGGL(clip_finalize_kernel, dim3(nseg), dim3(kClipThreads), 0, stream, seg_tile0, partials, max_norm,
                      kind, p, coefs, totals_out);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || total_tiles == 0) return e;
+  if (e != hipSuccess || total_tiles == 0 || !scale) return e;
   if (dt == kBF16)
     hipLaunchKernelGGL(clip_scale_kernel<kBF16>, dim3(grid), dim3(kClipThreads), 0, stream, descs, tile_prefix, n,
                        total_tiles, coefs);

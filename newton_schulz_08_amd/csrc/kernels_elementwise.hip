@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
                                                               const int* __restrict__ prefix, int nmat,
                                                               int total_tiles, float* __restrict__ partials,
                                                               int mode, float mu, int nesterov, float lr,
-                                                              float decay) {
+                                                              float decay, const float* __restrict__ gcoef) {
   using T = typename Elem<DT>::T;
   __shared__ float tile[kEwTile][kEwTile + 1];
   __shared__ float rowsum[4][16];   // row sums of the tile's four 16 x 64 blocks
@@ -211,6 +211,12 @@ __global__ __launch_bounds__(kEwThreads) void prologue_kernel(const MatDesc* __r
       const int r = r0 + rl, c = c0 + cl;
       float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (in[pass]) {
+        if (gcoef) {
+          // clipped gradient (training guide, "梯度裁剪": clipping precedes momentum)
+          const float cf = gcoef[d.clip_seg];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) g[pass][e] *= cf;
+        }
         if (mode == kModeMuon) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -381,15 +387,15 @@ __global__ __launch_bounds__(kEwThreads) void apply_x0_kernel(const MatDesc* __r
 }  // namespace
 
 hipError_t launch_prologue(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
-                           float* partials, int mode, float mu, int nesterov, float lr, float decay, int grid,
-                           hipStream_t stream) {
+                           float* partials, int mode, float mu, int nesterov, float lr, float decay,
+                           const float* gcoef, int grid, hipStream_t stream) {
   if (total_tiles <= 0) return hipSuccess;
   if (dt == kBF16)
     hipLaunchKernelGGL(prologue_kernel<kBF16>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
-                       total_tiles, partials, mode, mu, nesterov, lr, decay);
+                       total_tiles, partials, mode, mu, nesterov, lr, decay, gcoef);
   else
     hipLaunchKernelGGL(prologue_kernel<kF32>, dim3(grid), dim3(kEwThreads), 0, stream, descs, tile_prefix, nmat,
-                       total_tiles, partials, mode, mu, nesterov, lr, decay);
+                       total_tiles, partials, mode, mu, nesterov, lr, decay, gcoef);
   return hipGetLastError();
 }
 

@@ -19,9 +19,11 @@ struct SegTable {
 // Fused momentum / Nesterov / norm partials / small-matrix update / iterate
 // materialisation, over `total_tiles` 64x64 tiles of all matrices.
 // Small-route weight update: p <- p * decay + step_lr * Y with decay = 1 - lr wd.
+// gcoef: NULL, or per-segment clipping coefficients; matrix i's gradient is
+// then read as gcoef[clip_seg] * g (in fp32, never rounded back).
 hipError_t launch_prologue(int dt, const MatDesc* descs, const int* tile_prefix, int nmat, int total_tiles,
-                           float* partials, int mode, float mu, int nesterov, float lr, float decay, int grid,
-                           hipStream_t stream);
+                           float* partials, int mode, float mu, int nesterov, float lr, float decay,
+                           const float* gcoef, int grid, hipStream_t stream);
 
 // Per-matrix sum of the prologue partials -> norm, 1/(norm+eps), squared.
 hipError_t launch_norm_finalize(const MatDesc* descs, const int* tile_prefix, int nmat, const float* partials,

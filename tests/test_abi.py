@@ -277,3 +277,61 @@ def test_adamw_workspace_and_validation(lib):
                                 None) == E.DMUON_OK
     if torch.cuda.device_count() == 0:
         assert call(ws=0x10000000) == E.DMUON_ERR_NO_DEVICE
+
+
+def test_noalloc_rejects_oversized_sets_before_device_work(lib):
+    E = _lib
+    shapes = ((4096, 4096), (4096, 4096))
+    need = _ws(lib, shapes, dt=1)[1]
+    assert need > E.DMUON_NOALLOC_SCRATCH_BYTES
+    rows = (ctypes.c_int64 * 2)(4096, 4096)
+    P = (ctypes.c_void_p * 2)
+    st = lib.dmuon_muon_step_noalloc(2, P(0x1000, 0x2000), P(0x3000, 0x4000), P(0x5000, 0x6000), rows, rows, 1, 5,
+                                     None, ctypes.c_float(0.95), 1, ctypes.c_float(0.02), ctypes.c_float(0.0), 0,
+                                     None, None, None, None)
+    assert st == E.DMUON_ERR_WORKSPACE
+    assert "DMUON_NOALLOC_SCRATCH_BYTES" in _lib.last_error()
+    # the same argument checks as dmuon_muon_step run first
+    st = lib.dmuon_muon_step_noalloc(2, P(0x1000, 0x1000), P(0x3000, 0x4000), P(0x5000, 0x6000), rows, rows, 1, 5,
+                                     None, ctypes.c_float(0.95), 1, ctypes.c_float(0.02), ctypes.c_float(0.0), 0,
+                                     None, None, None, None)
+    assert st == E.DMUON_ERR_INVALID_ARG and "alias" in _lib.last_error()
+
+
+def _summary(lib, shapes, dt=1, steps=5, muon=1, cfg=None):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * n)(*[s[0] for s in shapes])
+    cols = (ctypes.c_int64 * n)(*[s[1] for s in shapes])
+    need = ctypes.c_size_t(0)
+    c = ctypes.byref(cfg) if cfg is not None else None
+    assert lib.dmuon_plan_summary(n, rows, cols, dt, c, steps, muon, None, 0, ctypes.byref(need)) == 0
+    buf = ctypes.create_string_buffer(need.value)
+    assert lib.dmuon_plan_summary(n, rows, cols, dt, c, steps, muon, buf, need.value, None) == 0
+    return buf.value.decode(), need.value, (n, rows, cols, c)
+
+
+def test_plan_summary(lib):
+    """The plan text names the routes, shape groups, orientation counts, K
+    slices and launches, with the algorithmic flops of one Newton-Schulz step
+    (the same count the benchmark uses)."""
+    import bench
+    shapes = [(4096, 4096), (14336, 4096), (4096, 14336), (14336, 4096), (1024, 4096), (2048, 32), (512, 2048)]
+    text, need, args = _summary(lib, shapes)
+    lines = text.splitlines()
+    assert "7 matrices (bf16)" in lines[0] and "6 Newton-Schulz in 4 shape groups" in lines[0]
+    assert "(2 iterated on the transpose), 1 elementwise" in lines[0]
+    assert "group 0: 3 x padded 4096 x 14336 (2 transposed)" in lines[1]
+    assert "K 2048 in 8 slices" in text                      # the 512 x 2048 matrix
+    assert "1 Gram launch(es) + 1 slice-sum launch(es), 1 update launch(es)" in text
+    syrk, gemm = bench.ns_flops([s for s in shapes if s[0] * s[1] >= 100000], 1)
+    assert f"{syrk + gemm:.4g} flop algorithmic" in text
+    # ns_batched plans orthogonalise every matrix; truncation keeps the NUL
+    assert "7 Newton-Schulz" in _summary(lib, shapes, muon=0)[0]
+    small = ctypes.create_string_buffer(16)
+    n, rows, cols, c = args
+    assert lib.dmuon_plan_summary(n, rows, cols, 1, c, 5, 1, small, 16, None) == 0
+    assert small.value.decode() == text[:15]
+    assert lib.dmuon_plan_summary(n, rows, cols, 1, c, -1, 1, None, 0, None) == _lib.DMUON_ERR_INVALID_ARG
+    direct = _cfg(backend=1)
+    assert "Gram 136 lower-triangle tiles each" in _summary(lib, [(4096, 4096)])[0]
+    assert "Gram 256 full tiles each" in _summary(lib, [(4096, 4096)], cfg=direct)[0]

@@ -594,3 +594,130 @@ def test_side_stream_allocations_outlive_the_call():
         _, _, uw, _ = oracle.muon_step([to_host_f64(p0[i])], [xs[i].as_f64()], [np.zeros(s)], f32_mu(0.95), True, 5,
                                        0.02)
         assert rel_fro(to_host_f64(u[i]), uw[0]) <= TOL["bf16"], s
+
+
+# ------------------------------------------------------------------ logging, checkpoint / resume
+def test_dmuon_log_prints_each_new_plan_once(monkeypatch, capfd):
+    """DMUON_LOG=1: a call prints its plan (dmuon_plan_summary's text) to
+    stderr when the plan differs from the last one printed, so a training loop
+    logs it once (the training guide's INFO summary, "日志与调试")."""
+    shapes = [(333, 777), (777, 333)]
+    x = [torch.randn(s, device="cuda") for s in shapes]
+    monkeypatch.setenv("DMUON_LOG", "1")
+    capfd.readouterr()
+    nsa.ns_batched(x, ns_steps=3)
+    nsa.ns_batched(x, ns_steps=3)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert err.count("dmuon plan:") == 1, err
+    assert nsa.plan_summary(shapes, torch.float32, 3, muon=False) in err
+    nsa.ns_batched(x[:1], ns_steps=3)
+    torch.cuda.synchronize()
+    assert capfd.readouterr().err.count("dmuon plan:") == 1
+    monkeypatch.setenv("DMUON_LOG", "0")
+    nsa.ns_batched(x, ns_steps=3)
+    torch.cuda.synchronize()
+    assert "dmuon plan:" not in capfd.readouterr().err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_checkpoint_resume_is_bitwise(dtype, tmp_path):
+    """Training guide, "相关文档" (检查点: saving and loading training
+    state).  The Muon state is the parameters and the momentum buffers; the
+    library keeps nothing between calls.  One step, a checkpoint through
+    torch.save, a load (weights_only) into fresh device tensors and a second
+    step with a fresh workspace must give bitwise the parameters and momentum
+    of two uninterrupted steps."""
+    shapes = [(600, 1100), (1100, 600), (40, 60)]
+    cfg = _adhoc(shapes, dtype, 250 + (dtype == "bf16"))
+    g1 = [to_device(gen.draw_matrix(cfg, i, gen.GRAD)) for i in range(3)]
+    g2 = [to_device(gen.draw_matrix(cfg, i, gen.GRAD2)) for i in range(3)]
+    p0 = [to_device(gen.draw_matrix(cfg, i, gen.WEIGHT)) for i in range(3)]
+    # uninterrupted
+    pa = [t.clone() for t in p0]
+    ba = [torch.zeros(s, device="cuda") for s in shapes]
+    first = nsa.MuonStep(pa, g1, ba)
+    first()
+    nsa.MuonStep(pa, g2, ba, workspace=first.workspace)()
+    # interrupted after the first step
+    pb = [t.clone() for t in p0]
+    bb = [torch.zeros(s, device="cuda") for s in shapes]
+    nsa.MuonStep(pb, g1, bb)()
+    torch.cuda.synchronize()
+    path = tmp_path / "muon_state.pt"
+    torch.save({"params": [t.cpu() for t in pb], "momentum": [t.cpu() for t in bb]}, path)
+    del pb, bb
+    state = torch.load(path, weights_only=True)
+    pc = [t.cuda() for t in state["params"]]
+    bc = [t.cuda() for t in state["momentum"]]
+    nsa.MuonStep(pc, g2, bc)()
+    torch.cuda.synchronize()
+    for i, s in enumerate(shapes):
+        assert torch.equal(pc[i], pa[i]), s
+        assert torch.equal(bc[i], ba[i]), s
+
+
+# ------------------------------------------------------------------ clipping folded into the step
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("norm_type", [2.0, float("inf")])
+def test_clipped_step_against_oracle(dtype, norm_type):
+    """Training guide, "梯度裁剪": per-segment global p-norm clipping before
+    momentum and Newton-Schulz, folded into the step (dmuon_muon_step_clipped).
+    Against the oracle's clip_grad_norm_buckets followed by its muon_step:
+    segment totals; momentum within one fp32 ulp of mu b + fl32(g coef) with
+    the GPU's own coefficient; U within the tolerance (elementwise route: one
+    ulp of the Nesterov input); parameters faithful.  Two segments clip, the
+    third does not and must equal the plain step bitwise; the caller's
+    gradients are not modified."""
+    shapes = [(600, 1100), (1100, 600), (40, 60), (512, 768), (300, 400), (700, 300)]
+    segments = [0, 0, 1, 1, 2, 2]
+    cfg = _adhoc(shapes, dtype, 260 + (dtype == "bf16") + 2 * (norm_type == 2.0))
+    g = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(len(shapes))]
+    p0 = [gen.draw_matrix(cfg, i, gen.WEIGHT) for i in range(len(shapes))]
+    b0 = [gen.draw_matrix(cfg, i, gen.MOMENTUM) for i in range(len(shapes))]
+    g64 = [x.as_f64() for x in g]
+    _, want_tot = oracle.clip_grad_norm_buckets(g64, segments, [1.0, 1.0, 1.0], norm_type)
+    max_norm = [0.5 * want_tot[0], 0.1 * want_tot[1], 10.0 * want_tot[2]]
+    clipped64, tot64 = oracle.clip_grad_norm_buckets(g64, segments, max_norm, norm_type)
+    dg = [to_device(x) for x in g]
+    dg_before = [t.clone() for t in dg]
+    dp = [to_device(x) for x in p0]
+    db = [to_device(x) for x in b0]
+    du = [torch.full(x.values.shape, float("nan"), device="cuda") for x in g]
+    totals = torch.full((3,), float("nan"), device="cuda")
+    mu, lr = 0.9, 0.02
+    nsa.MuonStep(dp, dg, db, mu=mu, lr=lr, update_out=du, clip_max_norm=max_norm, clip_segments=segments,
+                 clip_norm_type=norm_type, clip_totals=totals)()
+    # the plain step on the same inputs, for the unclipped segment
+    pp = [to_device(x) for x in p0]
+    bp = [to_device(x) for x in b0]
+    up = [torch.full(x.values.shape, float("nan"), device="cuda") for x in g]
+    nsa.MuonStep(pp, dg, bp, mu=mu, lr=lr, update_out=up)()
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(dg, dg_before))
+    tot = totals.cpu().numpy().astype(np.float64)
+    for s in range(3):
+        assert abs(tot[s] - tot64[s]) <= 2e-6 * tot64[s], (s, tot[s], tot64[s])
+    mu32 = f32_mu(mu)
+    for i, sh in enumerate(shapes):
+        s = segments[i]
+        coef = np.float32(max_norm[s]) / (np.float32(tot[s]) + np.float32(1e-6))
+        coef = np.float32(1.0) if coef >= 1.0 else np.float32(coef)
+        g32 = (g[i].values.astype(np.float32) if dtype == "f32" else g64[i].astype(np.float32)) * coef
+        b_exact = mu32 * b0[i].as_f64() + g32.astype(np.float64)
+        bg = to_host_f64(db[i])
+        assert max_ulp_err_f32(bg, b_exact) <= 1.0, (sh, "momentum")
+        u = to_host_f64(du[i])
+        pw, _, uw, _ = oracle.muon_step([p0[i].as_f64()], [clipped64[i]], [b0[i].as_f64()], mu32, True, 5, lr)
+        if sh[0] * sh[1] < oracle.MIN_NS_NUMEL:
+            y = g32.astype(np.float64) + mu32 * bg
+            assert max_ulp_err_f32(u, y) <= 1.0, (sh, "elementwise update")
+        else:
+            err = rel_fro(u, uw[0])
+            assert err <= TOL[dtype], (sh, err)
+        check_update_faithful(to_host_f64(dp[i]), p0[i].as_f64(), u, lr, 1.0, dtype)
+        if s == 2:
+            assert coef == 1.0
+            assert torch.equal(du[i], up[i]) and torch.equal(dp[i], pp[i]) and torch.equal(db[i], bp[i]), sh
+        else:
+            assert coef < 1.0
