@@ -4,6 +4,7 @@ a graph, enqueues nothing, and leaves the library usable afterwards.
 Each call uploads its descriptors from host memory that lives only for the
 call, so a recorded copy would read freed memory when the graph is replayed;
 the library refuses instead of recording it."""
+import ctypes
 import warnings
 
 import pytest
@@ -51,6 +52,17 @@ def test_every_entry_point_refuses_capture():
     before = [t.clone() for t in (p, g, mom, x, out, m, v, pa, ga)]
 
     step = nsa.MuonStep([p], [g], [mom], ns_steps=3)
+    clipped = nsa.MuonStep([p], [g], [mom], ns_steps=3, clip_max_norm=0.5)
+    lib = nsa.load()
+
+    def noalloc():
+        P = ctypes.c_void_p * 1
+        rows, cols = (ctypes.c_int64 * 1)(256), (ctypes.c_int64 * 1)(512)
+        st = lib.dmuon_muon_step_noalloc(1, P(p.data_ptr()), P(g.data_ptr()), P(mom.data_ptr()), rows, cols,
+                                         _lib.DMUON_F32, 3, None, ctypes.c_float(0.95), 1, ctypes.c_float(0.02),
+                                         ctypes.c_float(0.0), 0, None, None, None,
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        _lib.check(st, "dmuon_muon_step_noalloc")
     ws_ns = nsa.alloc_workspace(nsa.ns_workspace_bytes([tuple(x.shape)], x.dtype))
     ws_clip = nsa.alloc_workspace(nsa.clip_grad_norm_workspace_bytes([ga.numel()]))
     ws_adam = nsa.alloc_workspace(nsa.adamw_step_workspace_bytes([pa.numel()]))
@@ -58,6 +70,8 @@ def test_every_entry_point_refuses_capture():
 
     calls = {
         "muon_step": lambda: step(),
+        "muon_step_clipped": lambda: clipped(),
+        "muon_step_noalloc": noalloc,
         "ns_batched": lambda: nsa.ns_batched([x], [out], ns_steps=3, workspace=ws_ns),
         "clip_grad_norm": lambda: nsa.clip_grad_norm_([ga], 0.5, workspace=ws_clip),
         "adamw_step": lambda: nsa.adamw_step_([pa], [ga], [m], [v], 1, workspace=ws_adam),
