@@ -78,12 +78,12 @@ def test_workspace_layout_exact(lib):
     # partials of its 16 x 64 blocks (1024 blocks, 4 KB), scales 16 B -- each
     # region 256-aligned -- then the fp32 iterate in two buffers that
     # alternate between steps, and A; m' = 512 is
-    # two tile rows, so the Gram's K = 2048 is cut into 8 slices whose fp32
+    # two tile rows, so the Gram's K = 2048 is cut into 4 slices whose fp32
     # 256x256 partial products (sized for all 2 x 2 tiles) follow
     st, nbytes = _ws(lib, [(512, 2048)], dt=0)
     assert st == 0
     mb = 512 * 2048 * 4
-    part = 2 * 2 * 8 * 256 * 256 * 4
+    part = 2 * 2 * 4 * 256 * 256 * 4
     assert nbytes == 256 + 256 + 4096 + 256 + 2 * mb + 512 * 512 * 4 + part
     # bf16: the iterate's low half + two operand copies (its high half, one per
     # step parity) + bf16 Gram
@@ -321,7 +321,7 @@ def test_plan_summary(lib):
     assert "7 matrices (bf16)" in lines[0] and "6 Newton-Schulz in 4 shape groups" in lines[0]
     assert "(2 iterated on the transpose), 1 elementwise" in lines[0]
     assert "group 0: 3 x padded 4096 x 14336 (2 transposed)" in lines[1]
-    assert "K 2048 in 8 slices" in text                      # the 512 x 2048 matrix
+    assert "K 2048 in 4 slices" in text                      # the 512 x 2048 matrix
     assert "1 Gram launch(es) + 1 slice-sum launch(es), 1 update launch(es)" in text
     syrk, gemm = bench.ns_flops([s for s in shapes if s[0] * s[1] >= 100000], 1)
     assert f"{syrk + gemm:.4g} flop algorithmic" in text

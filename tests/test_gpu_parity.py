@@ -534,12 +534,13 @@ def test_more_than_sixteen_shape_groups(dtype):
     """One call with 21 distinct padded shapes (m', n') = (256 a, 256 b), both
     orientations, ragged: every contraction launch table holds at most 16
     shape groups, so each product runs as two launches with their own tile
-    numbering and XCD mapping.  17 of the 18 groups with m' <= 512 have their
-    Gram cut into K slices (K = 11 * 256 has no slice count in 2..8), so split
-    segments land in both Gram launches and the slice sums need two launches
-    as well.  Every matrix against the oracle."""
+    numbering and XCD mapping.  The 18 groups with m' <= 512 (every b has a
+    slice count in 2..4) have their Gram cut into K slices, so split segments
+    land in both Gram launches and the slice sums need two launches as well.
+    Every matrix against the oracle."""
     shapes = []
-    for a, bs in ((1, range(2, 11)), (2, range(3, 12)), (3, range(4, 7))):
+    bs_split = (2, 3, 4, 6, 8, 9, 10, 12, 14)
+    for a, bs in ((1, bs_split), (2, bs_split), (3, range(4, 7))):
         for b in bs:
             r, c = 256 * a - 5 * a, 256 * b - 11
             shapes.append((r, c) if (a + b) % 2 else (c, r))
