@@ -6,7 +6,9 @@
 //
 //   syrk_kernel    A = alpha * X X^T      lower-triangle 256x256 tiles only; each
 //                                         off-diagonal tile is also stored
-//                                         transposed into the upper triangle.
+//                                         transposed into the upper triangle, and
+//                                         a diagonal tile's upper-right quadrant
+//                                         is its lower-left one transposed.
 //   ns_gemm_kernel X <- g * (c0 X + c1 A X)    fused epilogue (blog's cubic map:
 //                                         c0 = 1.5, c1 = -0.5); on the last step
 //                                         it writes the update into the caller's
@@ -225,12 +227,15 @@ struct WaveGrid {
 // multiplied (one per call, spread between MFMAs).  after_last_barrier() runs
 // once every wave has read its last operand fragment: from then on the caller
 // owns all of the LDS, while the final MFMAs are still in flight.
+// kIdle: the caller does not need this wave's 128 x 64 block of the product.
+// The wave still issues its share of every stage's loads and joins every
+// barrier, but reads no fragments and runs no MFMAs; its acc is left as is.
 //
 // Global -> LDS: global_load_lds_dwordx4 writes lane l's 16 bytes to
 // LDS[M0 + 16 l], so one wave instruction fills 1 KB of a stage.  Each lane
 // fetches the source chunk that belongs in its slot of the XOR-swizzled
 // layout the fragment reads expect, so there is no VGPR staging.
-template <int DT, int kWaves, bool QN, typename BeforeLastStage, typename AfterLastBarrier>
+template <int DT, int kWaves, bool QN, bool kIdle = false, typename BeforeLastStage, typename AfterLastBarrier>
 __device__ __forceinline__ void block_product(const char* __restrict__ P0, int ldp_bytes,
                                               const char* __restrict__ Q0, int ldq_bytes, int kbytes, char* lds,
                                               f32x16 (&acc)[4][WaveGrid<kWaves>::kBN],
@@ -336,6 +341,7 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
   };
   // read i of a sub-step, in the order the MFMAs need them: fb[0], fa[0], fb[1..], fa[1..]
   auto read_one = [&](int stage, int s, int rs, int i) {
+    if constexpr (kIdle) return;
     const int co = (((2 * s + lh) ^ sw) << 4);
     const char* base = lds + stage * kStageBytes + frag_row + co;
     if (i == 0) read_q(stage, s, rs, 0);
@@ -357,6 +363,7 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
     }
   };
   auto mfma_one = [&](int rs, int j) {
+    if constexpr (kIdle) return;
     const int mi = j / kBN, ni = j % kBN;
     if constexpr (DT == kBF16) {
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[rs][ni], fa[rs][mi], acc[mi][ni], 0, 0, 0);
@@ -613,6 +620,9 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   const char* xs = static_cast<const char*>(square ? d.a : ((step & 1) ? d.xs1 : d.xs0));
   const int kdim = square ? mp : np;
   const long ld = static_cast<long>(kdim) * EB;
+  // a lower-triangle tile on the diagonal (a full-Gram launch computes every
+  // tile whole)
+  const bool diag = tr.bi == tr.bj && !tr.full;
 
   f32x16 acc[4][kBN];
 #pragma unroll
@@ -623,10 +633,16 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   if (!reduce) {
     // K slice of this block: all of K, or 1 / ksplit of it (a multiple of 256)
     const int klen = kdim / tr.ksplit;
-    const long koff = static_cast<long>(tr.slice) * klen * EB;
-    block_product<DT, kWaves, false>(xs + static_cast<long>(tr.bi) * kTile * ld + koff, ld,
-                                     xs + static_cast<long>(tr.bj) * kTile * ld + koff, ld, klen * EB, lds, acc,
-                                     [](int) {}, [] {});
+    const char* p = xs + static_cast<long>(tr.bi) * kTile * ld + static_cast<long>(tr.slice) * klen * EB;
+    const char* q = xs + static_cast<long>(tr.bj) * kTile * ld + static_cast<long>(tr.slice) * klen * EB;
+    // A diagonal tile's upper-right 128 x 128 quadrant is the transpose of its
+    // lower-left one, which the epilogue mirrors into place: the two waves
+    // that own that quadrant only help load
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (diag && wv / Grid::kWN == 0 && wv % Grid::kWN >= Grid::kWN / 2)
+      block_product<DT, kWaves, false, true>(p, ld, q, ld, klen * EB, lds, acc, [](int) {}, [] {});
+    else
+      block_product<DT, kWaves, false>(p, ld, q, ld, klen * EB, lds, acc, [](int) {}, [] {});
     if (tr.ksplit > 1) {
       store_partial(tr.part + static_cast<long>(tr.slice) * kPartialFloats, acc);
       return;
@@ -643,6 +659,9 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
   const bool mirror = tr.bi != tr.bj && !tr.full;
   __syncthreads();  // operand stages are free
+  // row half h = 0 of a diagonal tile holds only its left 128 columns (in
+  // 4-column chunks c < 32); half 1 supplies the rest as its transpose
+  const int halfc = diag ? 32 : 64;
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     if (wr == h) stage_acc(lds, acc, alpha);
@@ -653,6 +672,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
 #pragma unroll 4
       for (int k = 0; k < (128 * 64 / kThreads); ++k) {
         const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
+        if (h == 0 && c >= halfc) continue;
         float av[4];
         vld4(a_in + static_cast<long>(Rt + 128 * h + r) * mp + Ct + 4 * c, av);
         const float4 v4 = stage_ld4(lds, r, c);
@@ -665,14 +685,18 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
 #pragma unroll 4
     for (int k = 0; k < (128 * 64 / kThreads); ++k) {
       const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
+      if (h == 0 && c >= halfc) continue;
       const float4 v4 = stage_ld4(lds, r, c);
       const float v[4] = {v4.x, v4.y, v4.z, v4.w};
       vst4(a + static_cast<long>(Rt + 128 * h + r) * mp + Ct + 4 * c, v);
     }
-    if (mirror) {
+    if (mirror || (diag && h == 1)) {
       // transposed copy into the upper triangle: 8-row segments of columns
+      // (of a diagonal tile only the left 128, which land right of the
+      // diagonal block's upper half)
+      const int nseg = (mirror ? 256 : 128) * 16 / kThreads;
 #pragma unroll 2
-      for (int j = 0; j < (256 * 16 / kThreads); ++j) {
+      for (int j = 0; j < nseg; ++j) {
         const int q = tid + kThreads * j, sgi = q & 15, col = q >> 4;
         float v[8];
         stage_col8(lds, sgi, col, v);
