@@ -22,6 +22,7 @@
 namespace dmuon {
 
 constexpr int kTile = 256;           // MFMA block tile (rows and cols)
+constexpr int kSmallTile = 128;      // block tile of the fp32 kernels for m' <= 2 kTile
 constexpr int kEwTile = 64;          // elementwise tile of a transposed (tall) matrix: 64 x 64
 constexpr int kEwRowTileRows = 16;   // elementwise tile of every other matrix: 16 x 256
 constexpr int kEwRowTileCols = 256;
@@ -75,7 +76,8 @@ struct alignas(16) Segment {
   int ntiles;         // count * tiles_per_mat
   int tiles_per_mat;
   int mat0;           // first entry in the NS descriptor list
-  int tm, tn;         // tile grid: rows, cols of 256-tiles (SYRK: tm == tn)
+  int tm, tn;         // tile grid: rows, cols of the launch's tiles (kTile, or kSmallTile for the
+                      // small fp32 kernels; SYRK: tm == tn)
   int kdim;           // contraction length in elements
   int full;           // Gram only: 1 = every tile, no mirror (measurement ablation); 0 = lower triangle
   int ksplit;         // Gram only: > 1 = K cut into ksplit slices, summed by a second launch
@@ -84,8 +86,9 @@ struct alignas(16) Segment {
 };
 static_assert(sizeof(Segment) == 48, "Segment layout");
 
-// One fp32 256 x 256 partial product of a K slice.
+// One fp32 partial product of a K slice: a 256 x 256 tile, or a small 128 x 128 one.
 constexpr int kPartialFloats = 256 * 256;
+constexpr int kSmallPartialFloats = kSmallTile * kSmallTile;
 
 // Per-matrix scalars produced by the norm reduction.
 struct alignas(16) MatScale {

@@ -102,12 +102,15 @@ int resolve_ns_config(const dmuon_ns_config* cfg, int ns_steps, bool need_coeffs
 struct Group {
   int64_t mp, np;
   int first, count;   // range in the NS part of the descriptor order
+  bool small = false; // fp32 with m' <= 2 kTile: the 128 x 128 tile kernels
   int ks_gram = 1;    // K slices of the Gram product (and of the square product of a three-term map)
   int ks_square = 1;
   size_t off_part = 0;  // fp32 partial products of split Gram tiles
+  int64_t tile() const { return small ? kSmallTile : kTile; }
 };
 
-// K slices for the Gram product of a small matrix.  A matrix of at most two
+// K slices for the Gram product of a small bf16 matrix (fp32 ones use the
+// 128 x 128 tiles below).  A matrix of at most two
 // 256-tile rows has at most 3 lower-triangle tiles, so a launch over a few of
 // them occupies a few CUs for the whole of K; cutting K into up to 4 slices
 // (each a multiple of 256) spreads it out, and a second launch sums the
@@ -123,6 +126,18 @@ int gram_ksplit(int64_t tile_rows, int64_t k) {
     if (units % d == 0) best = d;
   return best;
 }
+
+// fp32 groups of at most two 256-tile rows run on 128 x 128 tiles: a matrix
+// has up to 10 lower-triangle Gram tiles and 4 n'/128 update tiles, and an
+// fp32 tile keeps its CU busy 4x as long per K as a bf16 one.  The TinyMLP
+// set (12 matrices, 512 x 2048 wide) has 768 update tiles, three per CU,
+// where 256 x 256 tiles gave 192 for 256 CUs.
+bool small_group(int dt, int64_t mp) { return dt == kF32 && mp <= 2 * kTile; }
+
+// K slices of a small tile's Gram product: two when K is at least 1024 (the
+// TinyMLP set's 120 tiles of K = 2048 become 240 blocks, one per CU), else one.
+// A function of the shape alone, like gram_ksplit.
+int small_gram_ksplit(int64_t k) { return k >= 1024 ? 2 : 1; }
 
 struct Plan {
   int dt = kF32;
@@ -251,13 +266,15 @@ Plan make_plan(int count, const int64_t* rows, const int64_t* cols, int dt, bool
   // tile of the grid (the direct backend computes all of them); the Gram and
   // the square product run one after the other and share the region
   for (Group& g : pl.groups) {
-    const int64_t T = g.mp / kTile;
-    g.ks_gram = gram_ksplit(T, g.np);
-    g.ks_square = three_terms ? gram_ksplit(T, g.mp) : 1;
+    g.small = small_group(dt, g.mp);
+    const int64_t T = g.mp / g.tile();
+    g.ks_gram = g.small ? small_gram_ksplit(g.np) : gram_ksplit(T, g.np);
+    g.ks_square = !three_terms ? 1 : g.small ? small_gram_ksplit(g.mp) : gram_ksplit(T, g.mp);
     const int ks = std::max(g.ks_gram, g.ks_square);
     if (ks > 1) {
+      const size_t part = g.small ? kSmallPartialFloats : kPartialFloats;
       g.off_part = off;
-      off = align_up(off + sizeof(float) * kPartialFloats * static_cast<size_t>(T * T) * g.count * ks);
+      off = align_up(off + sizeof(float) * part * static_cast<size_t>(T * T) * g.count * ks);
     }
   }
   pl.total = std::max<size_t>(off, kAlign);
@@ -479,12 +496,14 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     Segment s;
     double flops;
   };
-  std::vector<SegSpec> syrk_segs, square_segs, gemm_segs;
+  // [0]: 256 x 256 tile kernels, [1]: the small fp32 ones
+  std::vector<SegSpec> syrk_segs[2], square_segs[2], gemm_segs[2];
   // the direct backend (or DMUON_NS_KERNEL=gemm) computes every Gram tile
   // instead of the lower triangle plus its mirror (same results)
   const bool full_gram = call.ns.direct;
   for (const Group& g : pl.groups) {
-    const int T = static_cast<int>(g.mp / kTile), TN = static_cast<int>(g.np / kTile);
+    const int T = static_cast<int>(g.mp / g.tile()), TN = static_cast<int>(g.np / g.tile());
+    const int kind = g.small ? 1 : 0;
     double sf = 0.0, qf = 0.0, gf = 0.0;
     for (int k = g.first; k < g.first + g.count; ++k) {
       const double mm = static_cast<double>(std::min(pl.mats[k].m, pl.mats[k].n));
@@ -503,12 +522,12 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     s.full = full_gram ? 1 : 0;
     s.ksplit = g.ks_gram;
     s.part = g.ks_gram > 1 ? reinterpret_cast<float*>(ws + g.off_part) : nullptr;
-    syrk_segs.push_back(SegSpec{s, sf});
+    syrk_segs[kind].push_back(SegSpec{s, sf});
     Segment sq = s;
     sq.kdim = static_cast<int>(g.mp);
     sq.ksplit = g.ks_square;
     sq.part = g.ks_square > 1 ? reinterpret_cast<float*>(ws + g.off_part) : nullptr;
-    square_segs.push_back(SegSpec{sq, qf});
+    square_segs[kind].push_back(SegSpec{sq, qf});
     Segment q{};
     q.mat0 = g.first;
     q.tiles_per_mat = T * TN;
@@ -516,12 +535,14 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     q.tm = T;
     q.tn = TN;
     q.kdim = static_cast<int>(g.mp);
-    gemm_segs.push_back(SegSpec{q, gf});
+    gemm_segs[kind].push_back(SegSpec{q, gf});
   }
   auto by_k = [](const SegSpec& a, const SegSpec& b) { return a.s.kdim > b.s.kdim; };
-  std::stable_sort(syrk_segs.begin(), syrk_segs.end(), by_k);
-  std::stable_sort(square_segs.begin(), square_segs.end(), by_k);
-  std::stable_sort(gemm_segs.begin(), gemm_segs.end(), by_k);
+  for (int kind = 0; kind < 2; ++kind) {
+    std::stable_sort(syrk_segs[kind].begin(), syrk_segs[kind].end(), by_k);
+    std::stable_sort(square_segs[kind].begin(), square_segs[kind].end(), by_k);
+    std::stable_sort(gemm_segs[kind].begin(), gemm_segs[kind].end(), by_k);
+  }
 
   // Launch tables of at most kMaxSegPerLaunch segments.  A split Gram segment
   // has one block per (tile, K slice) in the product launch; reduce tables
@@ -548,53 +569,63 @@ int run(const Plan& pl, const Call& call, void* workspace, hipStream_t stream) {
     }
     return out;
   };
-  const auto syrk_launches = batches(syrk_segs, false);
-  const auto syrk_reduces = batches(syrk_segs, true);
-  const auto square_launches = batches(square_segs, false);
-  const auto square_reduces = batches(square_segs, true);
-  const auto gemm_launches = batches(gemm_segs, false);
+  using Launches = std::vector<std::pair<SegTable, std::pair<int, double>>>;
+  Launches syrk_launches[2], syrk_reduces[2], square_launches[2], square_reduces[2], gemm_launches[2];
+  for (int kind = 0; kind < 2; ++kind) {
+    syrk_launches[kind] = batches(syrk_segs[kind], false);
+    syrk_reduces[kind] = batches(syrk_segs[kind], true);
+    square_launches[kind] = batches(square_segs[kind], false);
+    square_reduces[kind] = batches(square_segs[kind], true);
+    gemm_launches[kind] = batches(gemm_segs[kind], false);
+  }
   const bool three = call.ns.terms == 3;
+  // Gram (or square) launches of one kind: the product, then the slice sums
+  auto gram = [&](int kind, const Launches& prod, const Launches& sums, int cls, int square, float cq, float cl,
+                  int step, const char* what) -> int {
+    for (int reduce = 0; reduce < 2; ++reduce) {
+      for (const auto& L : reduce ? sums : prod) {
+        e = timed(cls, reduce ? 0.0 : L.second.second, 0.0, stream, [&] {
+          return kind ? launch_small_syrk(d_descs, L.first, L.second.first, d_scales, step, square, cq, cl, reduce,
+                                          stream)
+                      : launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, square, cq, cl, reduce,
+                                    stream);
+        });
+        if (e != hipSuccess)
+          return fail(DMUON_ERR_HIP, std::string(what) + (reduce ? " sum launch: " : " launch: ") + hipGetErrorString(e));
+      }
+    }
+    return DMUON_OK;
+  };
 
   for (int step = 0; step < call.ns_steps; ++step) {
     const std::array<float, 3>& c = call.ns.coeffs[step];
-    for (const auto& L : syrk_launches) {
-      e = timed(kKSyrk, L.second.second, 0.0, stream, [&] {
-        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 0, 0.0f, 0.0f, 0, stream);
-      });
-      if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk launch: ") + hipGetErrorString(e));
-    }
-    for (const auto& L : syrk_reduces) {
-      e = timed(kKSyrk, 0.0, 0.0, stream, [&] {
-        return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 0, 0.0f, 0.0f, 1, stream);
-      });
-      if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk sum launch: ") + hipGetErrorString(e));
+    for (int kind = 0; kind < 2; ++kind) {
+      const int st = gram(kind, syrk_launches[kind], syrk_reduces[kind], kKSyrk, 0, 0.0f, 0.0f, step, "syrk");
+      if (st != DMUON_OK) return st;
     }
     // a step whose c2 is zero (a two-term set inside a three-term schedule)
     // needs no square product
     const bool sq = three && c[2] != 0.0f;
     if (sq) {
       // B = c2 A A + c1 A
-      for (const auto& L : square_launches) {
-        e = timed(kKSquare, L.second.second, 0.0, stream, [&] {
-          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 1, c[2], c[1], 0, stream);
-        });
-        if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk square launch: ") + hipGetErrorString(e));
-      }
-      for (const auto& L : square_reduces) {
-        e = timed(kKSquare, 0.0, 0.0, stream, [&] {
-          return launch_syrk(dt, d_descs, L.first, L.second.first, d_scales, step, 1, c[2], c[1], 1, stream);
-        });
-        if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("syrk square sum launch: ") + hipGetErrorString(e));
+      for (int kind = 0; kind < 2; ++kind) {
+        const int st = gram(kind, square_launches[kind], square_reduces[kind], kKSquare, 1, c[2], c[1], step,
+                            "syrk square");
+        if (st != DMUON_OK) return st;
       }
     }
     const int last = (step + 1 == call.ns_steps) ? 1 : 0;
     const float cax = sq ? 1.0f : c[1];
-    for (const auto& L : gemm_launches) {
-      e = timed(kKGemm, L.second.second, 0.0, stream, [&] {
-        return launch_ns_gemm(dt, d_descs, L.first, L.second.first, d_scales, step, last, call.mode, call.lr,
-                              call.decay, c[0], cax, sq ? 1 : 0, stream);
-      });
-      if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("ns_gemm launch: ") + hipGetErrorString(e));
+    for (int kind = 0; kind < 2; ++kind) {
+      for (const auto& L : gemm_launches[kind]) {
+        e = timed(kKGemm, L.second.second, 0.0, stream, [&] {
+          return kind ? launch_small_gemm(d_descs, L.first, L.second.first, d_scales, step, last, call.mode, call.lr,
+                                          call.decay, c[0], cax, sq ? 1 : 0, stream)
+                      : launch_ns_gemm(dt, d_descs, L.first, L.second.first, d_scales, step, last, call.mode,
+                                       call.lr, call.decay, c[0], cax, sq ? 1 : 0, stream);
+        });
+        if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("ns_gemm launch: ") + hipGetErrorString(e));
+      }
     }
   }
   return DMUON_OK;
@@ -791,10 +822,10 @@ std::string plan_summary(const Plan& pl, const NsCfg& ns, int ns_steps, bool muo
                       "(%d iterated on the transpose), %d elementwise (numel < %d)\n",
                       muon ? "muon_step" : "ns_batched", pl.count, pl.dt == kBF16 ? "bf16" : "fp32", ns_steps,
                       pl.n_ns, pl.groups.size(), tall, pl.count - pl.n_ns, DMUON_MIN_NS_NUMEL);
-  int split = 0;
+  int split[2] = {0, 0}, groups[2] = {0, 0};   // [0]: 256 x 256 tiles, [1]: 128 x 128
   for (size_t i = 0; i < pl.groups.size(); ++i) {
     const Group& g = pl.groups[i];
-    const int64_t T = g.mp / kTile, TN = g.np / kTile;
+    const int64_t T = g.mp / g.tile(), TN = g.np / g.tile();
     double fl = 0.0;
     int gt = 0;
     for (int k = g.first; k < g.first + g.count; ++k) {
@@ -803,20 +834,21 @@ std::string plan_summary(const Plan& pl, const NsCfg& ns, int ns_steps, bool muo
       fl += mm * (mm + 1.0) * nn + 2.0 * mm * mm * nn + 3.0 * mm * nn;
       gt += pl.mats[k].tr ? 1 : 0;
     }
-    if (g.ks_gram > 1) ++split;
-    s += fmt("  group %zu: %d x padded %lld x %lld (%d transposed); Gram %lld %s tiles each, K %lld%s; "
+    ++groups[g.small];
+    if (g.ks_gram > 1) ++split[g.small];
+    s += fmt("  group %zu: %d x padded %lld x %lld (%d transposed); Gram %lld %s %lldx%lld tiles each, K %lld%s; "
              "update %lld tiles each; %.4g flop per NS step\n",
              i, g.count, static_cast<long long>(g.mp), static_cast<long long>(g.np), gt,
              static_cast<long long>(ns.direct ? T * T : T * (T + 1) / 2), ns.direct ? "full" : "lower-triangle",
-             static_cast<long long>(g.np), g.ks_gram > 1 ? fmt(" in %d slices", g.ks_gram).c_str() : "",
-             static_cast<long long>(T * TN), fl);
+             static_cast<long long>(g.tile()), static_cast<long long>(g.tile()), static_cast<long long>(g.np),
+             g.ks_gram > 1 ? fmt(" in %d slices", g.ks_gram).c_str() : "", static_cast<long long>(T * TN), fl);
   }
-  const size_t ng = pl.groups.size();
-  const size_t per = static_cast<size_t>(kMaxSegPerLaunch);
-  s += fmt("  per NS step: %zu Gram launch(es) + %zu slice-sum launch(es)%s, %zu update launch(es); "
+  const int per = kMaxSegPerLaunch;
+  auto launches = [per](const int (&n)[2]) { return (n[0] + per - 1) / per + (n[1] + per - 1) / per; };
+  s += fmt("  per NS step: %d Gram launch(es) + %d slice-sum launch(es)%s, %d update launch(es); "
            "%.4g flop algorithmic (Gram %.4g, update %.4g)\n",
-           (ng + per - 1) / per, (split + per - 1) / per, ns.terms == 3 ? " + the square launches" : "",
-           (ng + per - 1) / per, pl.syrk_flops + pl.gemm_flops, pl.syrk_flops, pl.gemm_flops);
+           launches(groups), launches(split), ns.terms == 3 ? " + the square launches" : "", launches(groups),
+           pl.syrk_flops + pl.gemm_flops, pl.syrk_flops, pl.gemm_flops);
   s += fmt("  prologue: %d tiles; workspace %zu bytes (%.2f GiB)\n", pl.total_tiles, pl.total,
            static_cast<double>(pl.total) / (1 << 30));
   return s;

@@ -108,8 +108,9 @@ struct TileRef {
 
 // reduce: the block is one tile of a split segment's summing launch (one
 // block per tile); otherwise a split segment has one block per (tile, slice),
-// the slices of a tile adjacent.
-__device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lower, bool reduce = false) {
+// the slices of a tile adjacent.  part_floats: the size of one partial product.
+__device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lower, bool reduce = false,
+                                          int part_floats = kPartialFloats) {
   int si = 0;
   while (si + 1 < st.nseg && st.seg[si + 1].tile0 <= block) ++si;
   const Segment& sg = st.seg[si];
@@ -121,7 +122,7 @@ __device__ __forceinline__ TileRef locate(const SegTable& st, int block, bool lo
     r.slice = local % r.ksplit;
     local /= r.ksplit;
   }
-  r.part = r.ksplit > 1 ? sg.part + static_cast<long>(local) * r.ksplit * kPartialFloats : nullptr;
+  r.part = r.ksplit > 1 ? sg.part + static_cast<long>(local) * r.ksplit * part_floats : nullptr;
   r.mat = sg.mat0 + local / sg.tiles_per_mat;
   const int t = local % sg.tiles_per_mat;
   r.kdim = sg.kdim;
@@ -894,6 +895,256 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   }
 }
 
+
+// ---------------------------------------------------------------- small fp32 tiles
+// fp32 matrices of at most two 256-tile rows (m' <= 512) give too few 256 x 256
+// tiles to occupy 256 CUs: the TinyMLP set's update is 192 of them, its Gram
+// 36.  The two kernels below compute the same products on 128 x 128 tiles (4x
+// the blocks): four waves in a 2 x 2 grid of 64 x 64 blocks, each 2 x 2
+// v_mfma_f32_32x32x2_f32 blocks.  An fp32 MFMA occupies its SIMD for 64 cycles,
+// so register-staged loads into padded LDS rows keep it fed.  The epilogues
+// work straight from the
+// accumulators (lane (li, lh), register 4 g + q of block (mi, ni) is
+// C[64 wr + 32 mi + li][64 wc + 32 ni + 8 g + 4 lh + q], as above).
+constexpr int kSmThreads = 256;
+// K per stage: two stages of 16 take 40 KB of LDS and at most 128 VGPRs, so
+// four workgroups share a CU and the TinyMLP set's 768 update tiles are all
+// resident at once (stages of 32 with two workgroups per CU: update launch
+// 0.131 against 0.125 ms, the Gram 0.045 against 0.047 ms, the step the same
+// to 1%)
+constexpr int kSmK = 16;
+constexpr int kSmWg = 4;                // workgroups per CU
+constexpr int kSmRowFloats = kSmK + 4;  // K-contiguous LDS row: + 4 floats (16-byte reads of 16 rows: distinct banks)
+constexpr int kSmCpr = kSmK / 4;        // 16-byte chunks per K-contiguous stage row
+constexpr int kSmLd = kSmK / 8;         // 16-byte loads per thread per operand and stage
+constexpr int kSmQnRowFloats = 136;     // row-major stage row: 128 floats + 8 (rows 4 apart land 32 banks apart)
+constexpr int kSmPFloats = kSmallTile * kSmRowFloats;
+constexpr int kSmStageFloats = 2 * kSmPFloats;   // P + Q (a row-major Q stage needs only kSmK * kSmQnRowFloats)
+static_assert(kSmK * kSmQnRowFloats <= kSmPFloats, "row-major stage fits the Q region");
+
+// acc[mi][ni] of wave (wr, wc) += its 64 x 64 block (rows 64 wr.., cols
+// 64 wc..) of P Q^T over K = klen, a multiple of kSmK.  P: 128 rows,
+// K-contiguous, pitch ldp floats.  Q: QN == false like P (its rows are output
+// columns); QN == true K rows of the 128 output columns, pitch ldq.  In each
+// stage, K index 8 u + 4 h + e is element e of the float4 that the lanes of
+// half h read for group u, for both operands alike, so every k is summed once.
+template <bool QN>
+__device__ __forceinline__ void small_product(const float* __restrict__ P, long ldp, const float* __restrict__ Q,
+                                              long ldq, int klen, float* lds, f32x16 (&acc)[2][2]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lh = lane >> 5;
+  // K-contiguous operands: thread t loads chunk t % kSmCpr of rows
+  // t / kSmCpr + (256 / kSmCpr) j; a row-major Q: 16 bytes at column 4 (t & 31)
+  // of K rows (t >> 5) + 8 j
+  f32v4 rp[kSmLd], rq[kSmLd];
+  const int crow = t / kSmCpr, cch = 4 * (t % kSmCpr);
+  constexpr int kRowStep = kSmThreads / kSmCpr;
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < kSmLd; ++j) {
+      rp[j] = *gmem(reinterpret_cast<const f32v4*>(P + static_cast<long>(crow + kRowStep * j) * ldp + k0 + cch));
+      if constexpr (QN)
+        rq[j] = *gmem(reinterpret_cast<const f32v4*>(Q + static_cast<long>(k0 + (t >> 5) + 8 * j) * ldq + 4 * (t & 31)));
+      else
+        rq[j] = *gmem(reinterpret_cast<const f32v4*>(Q + static_cast<long>(crow + kRowStep * j) * ldq + k0 + cch));
+    }
+  };
+  auto store = [&](float* st) {
+#pragma unroll
+    for (int j = 0; j < kSmLd; ++j) {
+      *reinterpret_cast<f32v4*>(st + (crow + kRowStep * j) * kSmRowFloats + cch) = rp[j];
+      if constexpr (QN)
+        *reinterpret_cast<f32v4*>(st + kSmPFloats + ((t >> 5) + 8 * j) * kSmQnRowFloats + 4 * (t & 31)) = rq[j];
+      else
+        *reinterpret_cast<f32v4*>(st + kSmPFloats + (crow + kRowStep * j) * kSmRowFloats + cch) = rq[j];
+    }
+  };
+  auto compute = [&](const float* st) {
+#pragma unroll
+    for (int u = 0; u < kSmK / 8; ++u) {
+      f32v4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = *reinterpret_cast<const f32v4*>(st + (64 * wr + 32 * i + li) * kSmRowFloats + 8 * u + 4 * lh);
+        if constexpr (QN) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            fb[i][e] = st[kSmPFloats + (8 * u + 4 * lh + e) * kSmQnRowFloats + 64 * wc + 32 * i + li];
+        } else {
+          fb[i] = *reinterpret_cast<const f32v4*>(st + kSmPFloats + (64 * wc + 32 * i + li) * kSmRowFloats + 8 * u +
+                                                  4 * lh);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[ni][e], fa[mi][e], acc[mi][ni], 0, 0, 0);
+    }
+  };
+  // two stages: stage s + 1's loads are in flight while stage s is multiplied
+  const int ns = klen / kSmK;
+  load(0);
+  store(lds);
+  __syncthreads();
+  for (int s = 0; s < ns; ++s) {
+    if (s + 1 < ns) load((s + 1) * kSmK);
+    compute(lds + (s & 1) * kSmStageFloats);
+    if (s + 1 < ns) store(lds + ((s + 1) & 1) * kSmStageFloats);
+    __syncthreads();
+  }
+}
+
+// A split small tile's partial product, by thread as for the 256 tiles.
+__device__ __forceinline__ void small_store_partial(float* part, const f32x16 (&acc)[2][2]) {
+  f32v4* dst = reinterpret_cast<f32v4*>(part) + threadIdx.x;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& a = acc[b >> 1][b & 1];
+      *gmem(dst + (b * 4 + g) * kSmThreads) = f32v4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+    }
+}
+
+__device__ __forceinline__ void small_add_partial(const float* part, f32x16 (&acc)[2][2]) {
+  const f32v4* src = reinterpret_cast<const f32v4*>(part) + threadIdx.x;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32v4 v = *gmem(src + (b * 4 + g) * kSmThreads);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[b >> 1][b & 1][4 * g + e] += v[e];
+    }
+}
+
+// One caller element of the last step (the transposed write of a tall matrix):
+// the same arithmetic as write_caller.
+__device__ __forceinline__ void write_caller1(const MatDesc& d, int mode, float step_lr, float decay, int orow,
+                                              int ocol, float u) {
+  if (orow >= d.m || ocol >= d.n) return;
+  const long o = static_cast<long>(orow) * d.n + ocol;
+  float* p = static_cast<float*>(d.p);
+  if (mode == kModeMuon) {
+    gmem(p)[o] = fmaf(step_lr, u, gmem(p)[o] * decay);
+    if (d.upd) gmem(d.upd)[o] = u;
+  } else {
+    gmem(p)[o] = u;
+  }
+}
+
+// The Gram product on 128 x 128 tiles (fp32): as syrk_kernel, with diagonal
+// tiles computed whole.
+__global__ __launch_bounds__(kSmThreads, kSmWg) void small_syrk_kernel(const MatDesc* __restrict__ descs, SegTable st,
+                                                                   const MatScale* __restrict__ scales, int step,
+                                                                   int square, float cq, float cl, int reduce) {
+  __shared__ __attribute__((aligned(16))) float lds[2 * kSmStageFloats];
+  const TileRef tr = locate(st, blockIdx.x, true, reduce != 0, kSmallPartialFloats);
+  const MatDesc& d = descs[tr.mat];
+  const int mp = d.mp;
+  const float* xs = static_cast<const float*>(square ? d.a : ((step & 1) ? d.xs1 : d.xs0));
+  const int kdim = square ? mp : d.np;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b >> 1][b & 1] = f32x16{};
+  if (!reduce) {
+    const int klen = kdim / tr.ksplit;
+    const long koff = static_cast<long>(tr.slice) * klen;
+    small_product<false>(xs + static_cast<long>(tr.bi) * kSmallTile * kdim + koff, kdim,
+                         xs + static_cast<long>(tr.bj) * kSmallTile * kdim + koff, kdim, klen, lds, acc);
+    if (tr.ksplit > 1) {
+      small_store_partial(tr.part + static_cast<long>(tr.slice) * kSmallPartialFloats, acc);
+      return;
+    }
+  } else {
+    for (int s = 0; s < tr.ksplit; ++s) small_add_partial(tr.part + static_cast<long>(s) * kSmallPartialFloats, acc);
+  }
+
+  const float alpha = square ? cq : (step == 0 ? scales[tr.mat].c2 : 1.0f);
+  float* out = static_cast<float*>(square ? d.b : d.a);
+  const float* a_in = static_cast<const float*>(d.a);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lh = lane >> 5;
+  const bool mirror = tr.bi != tr.bj && !tr.full;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = tr.bi * kSmallTile + 64 * wr + 32 * mi + li;
+        const int c = tr.bj * kSmallTile + 64 * wc + 32 * ni + 8 * g + 4 * lh;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[mi][ni][4 * g + q] * alpha;
+        if (square) {
+          // B = cq A A + cl A
+          float av[4];
+          vld4(a_in + static_cast<long>(r) * mp + c, av);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(cl, av[q], v[q]);
+        }
+        vst4(out + static_cast<long>(r) * mp + c, v);
+        if (mirror) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) gmem(out)[static_cast<long>(c + q) * mp + r] = v[q];
+        }
+      }
+}
+
+// The update on 128 x 128 tiles (fp32): as ns_gemm_kernel.
+__global__ __launch_bounds__(kSmThreads, kSmWg) void small_gemm_kernel(const MatDesc* __restrict__ descs, SegTable st,
+                                                                   const MatScale* __restrict__ scales, int step,
+                                                                   int last, int mode, float lr, float decay,
+                                                                   float cx, float cax, int poly) {
+  __shared__ __attribute__((aligned(16))) float lds[2 * kSmStageFloats];
+  const TileRef tr = locate(st, blockIdx.x, false);
+  const MatDesc& d = descs[tr.mat];
+  const int mp = d.mp, np = d.np;
+  const float* m = static_cast<const float*>(poly ? d.b : d.a);
+  // the iterate: read from this step's buffer, written to the other one
+  const float* xq = static_cast<const float*>((step & 1) ? d.xs1 : d.xs0);
+  float* xnext = static_cast<float*>((step & 1) ? d.xs0 : d.xs1);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b >> 1][b & 1] = f32x16{};
+  small_product<true>(m + static_cast<long>(tr.bi) * kSmallTile * mp, mp, xq + static_cast<long>(tr.bj) * kSmallTile,
+                      np, mp, lds, acc);
+
+  const float gamma = (step == 0) ? scales[tr.mat].c : 1.0f;
+  const float step_lr = -lr * d.lr_scale;
+  const bool trn = d.tr != 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = tr.bi * kSmallTile + 64 * wr + 32 * mi + li;
+        const int c = tr.bj * kSmallTile + 64 * wc + 32 * ni + 8 * g + 4 * lh;
+        float x[4], xn[4];
+        vld4(xq + static_cast<long>(r) * np + c, x);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xn[q] = gamma * (cx * x[q] + cax * acc[mi][ni][4 * g + q]);
+        if (!last) {
+          vst4(xnext + static_cast<long>(r) * np + c, xn);
+        } else if (!trn) {
+          write_caller<float, 4>(d, mode, step_lr, decay, r, c, xn);
+        } else {
+          // tall: wide (r, c + q) is caller (c + q, r)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) write_caller1(d, mode, step_lr, decay, c + q, r, xn[q]);
+        }
+      }
+}
+
 }  // namespace
 
 hipError_t launch_syrk(int dt, const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales,
@@ -918,6 +1169,23 @@ hipError_t launch_ns_gemm(int dt, const MatDesc* descs, const SegTable& st, int 
   else
     hipLaunchKernelGGL(ns_gemm_kernel<kF32>, dim3(ntiles), dim3(kThreads), 0, stream, descs, st, scales, step, last,
                        mode, lr, decay, cx, cax, poly);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_syrk(const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales, int step,
+                             int square, float cq, float cl, int reduce, hipStream_t stream) {
+  if (ntiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(small_syrk_kernel, dim3(ntiles), dim3(kSmThreads), 0, stream, descs, st, scales, step, square,
+                     cq, cl, reduce);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_gemm(const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales, int step,
+                             int last, int mode, float lr, float decay, float cx, float cax, int poly,
+                             hipStream_t stream) {
+  if (ntiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(small_gemm_kernel, dim3(ntiles), dim3(kSmThreads), 0, stream, descs, st, scales, step, last, mode,
+                     lr, decay, cx, cax, poly);
   return hipGetLastError();
 }
 

@@ -52,4 +52,12 @@ hipError_t launch_ns_gemm(int dt, const MatDesc* descs, const SegTable& st, int 
                           int step, int last, int mode, float lr, float decay, float cx, float cax, int poly,
                           hipStream_t stream);
 
+// The same two products for fp32 matrices with m' <= 2 kTile, on 128 x 128
+// tiles (segments' tile grids and partial products in those tiles).
+hipError_t launch_small_syrk(const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales, int step,
+                             int square, float cq, float cl, int reduce, hipStream_t stream);
+hipError_t launch_small_gemm(const MatDesc* descs, const SegTable& st, int ntiles, const MatScale* scales, int step,
+                             int last, int mode, float lr, float decay, float cx, float cax, int poly,
+                             hipStream_t stream);
+
 }  // namespace dmuon

@@ -77,16 +77,18 @@ def test_workspace_layout_exact(lib):
     # one 512x2048 fp32 matrix: descriptor 128 B, prefix 8 B, the sum-of-squares
     # partials of its 16 x 64 blocks (1024 blocks, 4 KB), scales 16 B -- each
     # region 256-aligned -- then the fp32 iterate in two buffers that
-    # alternate between steps, and A; m' = 512 is
-    # two tile rows, so the Gram's K = 2048 is cut into 4 slices whose fp32
-    # 256x256 partial products (sized for all 2 x 2 tiles) follow
+    # alternate between steps, and A; an fp32 matrix with m' = 512 runs on
+    # 128 x 128 tiles, and its Gram's K = 2048 is cut into 2 slices whose fp32
+    # 128x128 partial products (sized for all 4 x 4 tiles) follow
     st, nbytes = _ws(lib, [(512, 2048)], dt=0)
     assert st == 0
     mb = 512 * 2048 * 4
-    part = 2 * 2 * 4 * 256 * 256 * 4
-    assert nbytes == 256 + 256 + 4096 + 256 + 2 * mb + 512 * 512 * 4 + part
+    small_part = 4 * 4 * 2 * 128 * 128 * 4
+    assert nbytes == 256 + 256 + 4096 + 256 + 2 * mb + 512 * 512 * 4 + small_part
     # bf16: the iterate's low half + two operand copies (its high half, one per
-    # step parity) + bf16 Gram
+    # step parity) + bf16 Gram; 256 x 256 tiles, two tile rows, so K = 2048 is
+    # cut into 4 slices of partial products sized for all 2 x 2 tiles
+    part = 2 * 2 * 4 * 256 * 256 * 4
     st, nb16 = _ws(lib, [(512, 2048)], dt=1)
     assert nb16 == 256 + 256 + 4096 + 256 + 512 * 2048 * (2 + 2 + 2) + 512 * 512 * 2 + part
     # a three-term polynomial adds the m' x m' buffer B = c1 A + c2 A^2 (its
@@ -333,5 +335,9 @@ def test_plan_summary(lib):
     assert small.value.decode() == text[:15]
     assert lib.dmuon_plan_summary(n, rows, cols, 1, c, -1, 1, None, 0, None) == _lib.DMUON_ERR_INVALID_ARG
     direct = _cfg(backend=1)
-    assert "Gram 136 lower-triangle tiles each" in _summary(lib, [(4096, 4096)])[0]
-    assert "Gram 256 full tiles each" in _summary(lib, [(4096, 4096)], cfg=direct)[0]
+    assert "Gram 136 lower-triangle 256x256 tiles each" in _summary(lib, [(4096, 4096)])[0]
+    # fp32 with m' <= 512: 128 x 128 tiles in launches of their own
+    t32 = _summary(lib, [(4096, 4096), (2048, 512)], dt=0)[0]
+    assert "Gram 10 lower-triangle 128x128 tiles each, K 2048 in 2 slices; update 64 tiles each" in t32
+    assert "2 Gram launch(es) + 1 slice-sum launch(es), 2 update launch(es)" in t32
+    assert "Gram 256 full 256x256 tiles each" in _summary(lib, [(4096, 4096)], cfg=direct)[0]

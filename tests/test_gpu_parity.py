@@ -320,8 +320,9 @@ def test_full_gram_ablation_matches(dtype, monkeypatch):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_small_gram_runs_in_k_slices(dtype):
     """A matrix of at most two 256-tile rows has its Gram product cut into K
-    slices and summed by a second launch (2 Gram launches per step); three
-    tile rows or more take one.  Split and unsplit shapes in one batch, the
+    slices and summed by a second launch (2 Gram launches per step; fp32 on
+    128 x 128 tiles, in 2 slices when n' >= 1024); three tile rows or more
+    take one.  Split and unsplit shapes in one batch, the
     square product of a three-term map, and the direct backend all meet the
     oracle."""
     shapes = [(300, 2100), (2100, 300), (256, 1024), (800, 1500)]
@@ -534,10 +535,13 @@ def test_more_than_sixteen_shape_groups(dtype):
     """One call with 21 distinct padded shapes (m', n') = (256 a, 256 b), both
     orientations, ragged: every contraction launch table holds at most 16
     shape groups, so each product runs as two launches with their own tile
-    numbering and XCD mapping.  The 18 groups with m' <= 512 (every b has a
-    slice count in 2..4) have their Gram cut into K slices, so split segments
-    land in both Gram launches and the slice sums need two launches as well.
-    Every matrix against the oracle."""
+    numbering and XCD mapping.  bf16: the 18 groups with m' <= 512 (every b
+    has a slice count in 2..4) have their Gram cut into K slices, so split
+    segments land in both Gram launches and the slice sums need two launches
+    as well.  fp32: those 18 groups run on 128 x 128 tiles in tables of their
+    own (16 + 2), the other 3 in one table, and the 14 small groups with
+    n' >= 1024 are split (one slice-sum table).  Every matrix against the
+    oracle."""
     shapes = []
     bs_split = (2, 3, 4, 6, 8, 9, 10, 12, 14)
     for a, bs in ((1, bs_split), (2, bs_split), (3, range(4, 7))):
@@ -552,8 +556,9 @@ def test_more_than_sixteen_shape_groups(dtype):
     res = run_muon(cfg, ns_steps=5)
     nsa.profile_enable(False)
     prof = nsa.profile_read()
-    assert prof["ns_gemm"]["launches"] == 2 * 5
-    assert prof["syrk"]["launches"] == 4 * 5          # two product tables + two slice-sum tables
+    gemm_tables = 2 if dtype == "bf16" else 3
+    assert prof["ns_gemm"]["launches"] == gemm_tables * 5
+    assert prof["syrk"]["launches"] == 4 * 5          # product and slice-sum tables, as above
     check_against_oracle(cfg, res, ns_steps=5)
 
 
