@@ -348,6 +348,30 @@ QUINTIC_FAST = (3.4445, -4.7750, 2.0315)
 QUINTIC_CLASSICAL = (1.875, -1.25, 0.375)
 
 
+def test_small_fp32_tiles():
+    """fp32 matrices with m' <= 512 run on 128 x 128 tiles in launches of their
+    own: m' of 256 and 512, both orientations, n' below 1024 (one Gram slice)
+    and above (two), ragged edges, beside a shape group on 256 x 256 tiles in
+    the same call.  The Muon step (the last Newton-Schulz step writing the
+    caller's parameters in their own orientation, update_out, weight decay,
+    Moonlight scale, non-zero momentum), the three-term square product and
+    the direct backend all meet the oracle, whole matrix and per tile."""
+    shapes = [(300, 900), (900, 300), (500, 2100), (2100, 500), (129, 1000), (250, 700), (700, 250), (513, 1500)]
+    cfg = _adhoc(shapes, "f32", 250)
+    print("[parity] small fp32 tiles", flush=True)
+    nsa.profile_read()
+    nsa.profile_enable(True)
+    res = run_muon(cfg, nonzero_buf=True, weight_decay=0.1, moonlight=True)
+    nsa.profile_enable(False)
+    prof = nsa.profile_read()
+    assert prof["ns_gemm"]["launches"] == 2 * 5          # a 128-tile and a 256-tile update table
+    assert prof["syrk"]["launches"] == 3 * 5             # both Gram tables and the small tiles' slice sums
+    check_against_oracle(cfg, res, weight_decay=0.1, moonlight=True)
+    for kw in ({"ns_coeffs": QUINTIC_FAST}, {"ns_backend": "direct"}):
+        res = run_muon(cfg, **kw)
+        check_against_oracle(cfg, res, ns_coeffs=kw.get("ns_coeffs"))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_weight_decay_and_moonlight_scale(dtype):
     """Decoupled decay and the 0.2*sqrt(max(m, n)) multiplier, on both routes."""
