@@ -212,7 +212,7 @@ struct WaveGrid {
   static constexpr int kThreadsPerBlock = 64 * kWaves;
   static constexpr int kWN = kWaves / 2;
   static constexpr int kBM = 4;                    // 128 rows
-  static constexpr int kBN = 256 / kWN / 32;       // 128 (4 waves) or 64 (8 waves) cols
+  static constexpr int kBN = 256 / kWN / 32;       // 32-column blocks per wave
   static constexpr int kLoadsPerOperand = 256 / kWaves / 8;  // 8-row wave loads per operand
 };
 
@@ -438,10 +438,9 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
   for (int j = 0; j < kMfma; ++j) mfma_one(1, j);
 }
 
-#ifndef DMUON_WAVES
-#define DMUON_WAVES 8
-#endif
-constexpr int kWaves = DMUON_WAVES;
+// Eight waves (two per SIMD) in a 2 x 4 grid of 128 x 64 blocks.  The load
+// maps and the update epilogue's vmcnt counts are written for this count.
+constexpr int kWaves = 8;
 using Grid = WaveGrid<kWaves>;
 constexpr int kBN = Grid::kBN;
 constexpr int kThreads = Grid::kThreadsPerBlock;
