@@ -228,15 +228,17 @@ struct WaveGrid {
 // multiplied (one per call, spread between MFMAs).  after_last_barrier() runs
 // once every wave has read its last operand fragment: from then on the caller
 // owns all of the LDS, while the final MFMAs are still in flight.
-// kIdle: the caller does not need this wave's 128 x 64 block of the product.
-// The wave still issues its share of every stage's loads and joins every
-// barrier, but reads no fragments and runs no MFMAs; its acc is left as is.
+// kMask: bit mi * kBN + ni set when the caller needs the wave's 32 x 32 block
+// (mi, ni); the wave runs only those blocks' MFMAs and reads only the
+// fragments they use, leaving the other accumulators as they are.  Every
+// wave, even one with no block to compute, still issues its share of every
+// stage's loads and joins every barrier.
 //
 // Global -> LDS: global_load_lds_dwordx4 writes lane l's 16 bytes to
 // LDS[M0 + 16 l], so one wave instruction fills 1 KB of a stage.  Each lane
 // fetches the source chunk that belongs in its slot of the XOR-swizzled
 // layout the fragment reads expect, so there is no VGPR staging.
-template <int DT, int kWaves, bool QN, bool kIdle = false, typename BeforeLastStage, typename AfterLastBarrier>
+template <int DT, int kWaves, bool QN, unsigned kMask = 0xFFu, typename BeforeLastStage, typename AfterLastBarrier>
 __device__ __forceinline__ void block_product(const char* __restrict__ P0, int ldp_bytes,
                                               const char* __restrict__ Q0, int ldq_bytes, int kbytes, char* lds,
                                               f32x16 (&acc)[4][WaveGrid<kWaves>::kBN],
@@ -341,8 +343,20 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
     }
   };
   // read i of a sub-step, in the order the MFMAs need them: fb[0], fa[0], fb[1..], fa[1..]
+  // fragments some needed block uses: P row block mi, Q column block ni
+  constexpr unsigned kRowBits = (1u << kBN) - 1u;
+  auto p_used = [](int mi) { return ((kMask >> (mi * kBN)) & kRowBits) != 0u; };
+  auto q_used = [](int ni) {
+    unsigned any = 0u;
+    for (int mi = 0; mi < 4; ++mi) any |= (kMask >> (mi * kBN + ni)) & 1u;
+    return any != 0u;
+  };
   auto read_one = [&](int stage, int s, int rs, int i) {
-    if constexpr (kIdle) return;
+    if (i == 0 || (i >= 2 && i < kBN + 1)) {
+      if (!q_used(i == 0 ? 0 : i - 1)) return;
+    } else if (!p_used(i == 1 ? 0 : i - kBN)) {
+      return;
+    }
     const int co = (((2 * s + lh) ^ sw) << 4);
     const char* base = lds + stage * kStageBytes + frag_row + co;
     if (i == 0) read_q(stage, s, rs, 0);
@@ -364,7 +378,7 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
     }
   };
   auto mfma_one = [&](int rs, int j) {
-    if constexpr (kIdle) return;
+    if (((kMask >> j) & 1u) == 0u) return;
     const int mi = j / kBN, ni = j % kBN;
     if constexpr (DT == kBF16) {
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[rs][ni], fa[rs][mi], acc[mi][ni], 0, 0, 0);
@@ -635,14 +649,20 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
     const int klen = kdim / tr.ksplit;
     const char* p = xs + static_cast<long>(tr.bi) * kTile * ld + static_cast<long>(tr.slice) * klen * EB;
     const char* q = xs + static_cast<long>(tr.bj) * kTile * ld + static_cast<long>(tr.slice) * klen * EB;
-    // A diagonal tile's upper-right 128 x 128 quadrant is the transpose of its
-    // lower-left one, which the epilogue mirrors into place: the two waves
-    // that own that quadrant only help load
+    // A diagonal tile needs only its 32 x 32 blocks on or below the block
+    // diagonal: the epilogue writes the others as transposes.  Block (R, C)
+    // of the tile (R = 4 wr + mi, C = kBN wc + ni) is needed when C <= R, so
+    // each wave runs one of four patterns (Grid: 2 x 4 waves of 4 x 2 blocks)
+    static_assert(Grid::kWN == 4 && kBN == 2, "diagonal block patterns");
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (diag && wv / Grid::kWN == 0 && wv % Grid::kWN >= Grid::kWN / 2)
-      block_product<DT, kWaves, false, true>(p, ld, q, ld, klen * EB, lds, acc, [](int) {}, [] {});
-    else
-      block_product<DT, kWaves, false>(p, ld, q, ld, klen * EB, lds, acc, [](int) {}, [] {});
+    const int band = (wv % Grid::kWN) - 2 * (wv / Grid::kWN);   // wave column pair relative to its row band
+    auto run = [&](auto mask) {
+      block_product<DT, kWaves, false, decltype(mask)::value>(p, ld, q, ld, klen * EB, lds, acc, [](int) {}, [] {});
+    };
+    if (!diag || band < 0) run(std::integral_constant<unsigned, 0xFFu>{});        // below the diagonal
+    else if (band == 0) run(std::integral_constant<unsigned, 0xFDu>{});           // all but block (0, 1)
+    else if (band == 1) run(std::integral_constant<unsigned, 0xD0u>{});           // blocks (2, 0), (3, 0), (3, 1)
+    else run(std::integral_constant<unsigned, 0x00u>{});                          // above the diagonal
     if (tr.ksplit > 1) {
       store_partial(tr.part + static_cast<long>(tr.slice) * kPartialFloats, acc);
       return;
@@ -659,9 +679,10 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
   const bool mirror = tr.bi != tr.bj && !tr.full;
   __syncthreads();  // operand stages are free
-  // row half h = 0 of a diagonal tile holds only its left 128 columns (in
-  // 4-column chunks c < 32); half 1 supplies the rest as its transpose
-  const int halfc = diag ? 32 : 64;
+  // A diagonal tile holds its 32 x 32 blocks on and below the block diagonal:
+  // rows write only those, and every strictly-lower block is also written
+  // transposed, which fills the rest.  blk(x) = x / 32.
+  auto upper = [&](int row, int col) { return diag && (col >> 5) > (row >> 5); };
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     if (wr == h) stage_acc(lds, acc, alpha);
@@ -672,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
 #pragma unroll 4
       for (int k = 0; k < (128 * 64 / kThreads); ++k) {
         const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
-        if (h == 0 && c >= halfc) continue;
+        if (upper(128 * h + r, 4 * c)) continue;
         float av[4];
         vld4(a_in + static_cast<long>(Rt + 128 * h + r) * mp + Ct + 4 * c, av);
         const float4 v4 = stage_ld4(lds, r, c);
@@ -685,19 +706,18 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
 #pragma unroll 4
     for (int k = 0; k < (128 * 64 / kThreads); ++k) {
       const int r = (tid >> 6) + (kThreads / 64) * k, c = tid & 63;
-      if (h == 0 && c >= halfc) continue;
+      if (upper(128 * h + r, 4 * c)) continue;
       const float4 v4 = stage_ld4(lds, r, c);
       const float v[4] = {v4.x, v4.y, v4.z, v4.w};
       vst4(a + static_cast<long>(Rt + 128 * h + r) * mp + Ct + 4 * c, v);
     }
-    if (mirror || (diag && h == 1)) {
+    if (mirror || diag) {
       // transposed copy into the upper triangle: 8-row segments of columns
-      // (of a diagonal tile only the left 128, which land right of the
-      // diagonal block's upper half)
-      const int nseg = (mirror ? 256 : 128) * 16 / kThreads;
+      // (of a diagonal tile only the strictly-lower blocks)
 #pragma unroll 2
-      for (int j = 0; j < nseg; ++j) {
+      for (int j = 0; j < 256 * 16 / kThreads; ++j) {
         const int q = tid + kThreads * j, sgi = q & 15, col = q >> 4;
+        if (diag && !upper(col, 128 * h + 8 * sgi)) continue;
         float v[8];
         stage_col8(lds, sgi, col, v);
         vst8(a + static_cast<long>(Ct + col) * mp + Rt + 128 * h + 8 * sgi, v);
