@@ -947,7 +947,9 @@ static_assert(kSmK * kSmQnRowFloats <= kSmPFloats, "row-major stage fits the Q r
 // columns); QN == true K rows of the 128 output columns, pitch ldq.  In each
 // stage, K index 8 u + 4 h + e is element e of the float4 that the lanes of
 // half h read for group u, for both operands alike, so every k is summed once.
-template <bool QN>
+// kMask: bit 2 mi + ni set when block (mi, ni) is needed (the others' MFMAs and
+// unused fragment reads are skipped; the wave still loads and joins barriers).
+template <bool QN, unsigned kMask = 0xFu>
 __device__ __forceinline__ void small_product(const float* __restrict__ P, long ldp, const float* __restrict__ Q,
                                               long ldq, int klen, float* lds, f32x16 (&acc)[2][2]) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -981,10 +983,12 @@ __device__ __forceinline__ void small_product(const float* __restrict__ P, long 
   auto compute = [&](const float* st) {
 #pragma unroll
     for (int u = 0; u < kSmK / 8; ++u) {
-      f32v4 fa[2], fb[2];
+      f32v4 fa[2] = {}, fb[2] = {};
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        fa[i] = *reinterpret_cast<const f32v4*>(st + (64 * wr + 32 * i + li) * kSmRowFloats + 8 * u + 4 * lh);
+        if ((kMask >> (2 * i)) & 3u)
+          fa[i] = *reinterpret_cast<const f32v4*>(st + (64 * wr + 32 * i + li) * kSmRowFloats + 8 * u + 4 * lh);
+        if (((kMask >> i) & 5u) == 0u) continue;
         if constexpr (QN) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -1000,7 +1004,8 @@ __device__ __forceinline__ void small_product(const float* __restrict__ P, long 
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[ni][e], fa[mi][e], acc[mi][ni], 0, 0, 0);
+            if ((kMask >> (2 * mi + ni)) & 1u)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[ni][e], fa[mi][e], acc[mi][ni], 0, 0, 0);
     }
   };
   // two stages: stage s + 1's loads are in flight while stage s is multiplied
@@ -1055,8 +1060,9 @@ __device__ __forceinline__ void write_caller1(const MatDesc& d, int mode, float 
   }
 }
 
-// The Gram product on 128 x 128 tiles (fp32): as syrk_kernel, with diagonal
-// tiles computed whole.
+// The Gram product on 128 x 128 tiles (fp32): as syrk_kernel.  A diagonal
+// tile computes only its 32 x 32 blocks on or below the block diagonal and
+// writes the strictly-lower ones transposed as well.
 __global__ __launch_bounds__(kSmThreads, kSmWg) void small_syrk_kernel(const MatDesc* __restrict__ descs, SegTable st,
                                                                    const MatScale* __restrict__ scales, int step,
                                                                    int square, float cq, float cl, int reduce) {
@@ -1070,11 +1076,21 @@ __global__ __launch_bounds__(kSmThreads, kSmWg) void small_syrk_kernel(const Mat
   f32x16 acc[2][2];
 #pragma unroll
   for (int b = 0; b < 4; ++b) acc[b >> 1][b & 1] = f32x16{};
+  const bool diag = tr.bi == tr.bj && !tr.full;
   if (!reduce) {
     const int klen = kdim / tr.ksplit;
     const long koff = static_cast<long>(tr.slice) * klen;
-    small_product<false>(xs + static_cast<long>(tr.bi) * kSmallTile * kdim + koff, kdim,
-                         xs + static_cast<long>(tr.bj) * kSmallTile * kdim + koff, kdim, klen, lds, acc);
+    const float* p = xs + static_cast<long>(tr.bi) * kSmallTile * kdim + koff;
+    const float* q = xs + static_cast<long>(tr.bj) * kSmallTile * kdim + koff;
+    // block (R, C) = (2 wr + mi, 2 wc + ni) of a diagonal tile is needed when C <= R
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int band = (wv & 1) - (wv >> 1);
+    auto run = [&](auto mask) {
+      small_product<false, decltype(mask)::value>(p, kdim, q, kdim, klen, lds, acc);
+    };
+    if (!diag || band < 0) run(std::integral_constant<unsigned, 0xFu>{});
+    else if (band == 0) run(std::integral_constant<unsigned, 0xDu>{});     // all but block (0, 1)
+    else run(std::integral_constant<unsigned, 0x0u>{});
     if (tr.ksplit > 1) {
       small_store_partial(tr.part + static_cast<long>(tr.slice) * kSmallPartialFloats, acc);
       return;
@@ -1107,8 +1123,12 @@ __global__ __launch_bounds__(kSmThreads, kSmWg) void small_syrk_kernel(const Mat
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = fmaf(cl, av[q], v[q]);
         }
+        // diagonal tile: blocks above the block diagonal are not computed,
+        // those below it are also written transposed
+        const int br = (r - tr.bi * kSmallTile) >> 5, bc = (c - tr.bj * kSmallTile) >> 5;
+        if (diag && bc > br) continue;
         vst4(out + static_cast<long>(r) * mp + c, v);
-        if (mirror) {
+        if (mirror || (diag && br > bc)) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) gmem(out)[static_cast<long>(c + q) * mp + r] = v[q];
         }
