@@ -25,9 +25,9 @@
 // LDS as K rows of 256 columns, and transposing LDS reads
 // (ds_read_b64_tr_b16; fp32: single-word reads) hand each lane the
 // K-consecutive values the MFMA expects.  Each 512-thread workgroup computes a 256x256
-// tile; its eight waves form a 2 x 4 grid of 128x64 blocks, each 4x2 blocks of
-// v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32), two waves
-// per SIMD.  K advances 128 bytes per stage (64 bf16 / 32 fp32) through a
+// tile; its eight waves form a 2 x 4 grid of 128x64 blocks, each 8x4 blocks of
+// v_mfma_f32_16x16x32_bf16 (bf16) or 4x2 blocks of v_mfma_f32_32x32x2_f32
+// (fp32), two waves per SIMD.  K advances 128 bytes per stage (64 bf16 / 32 fp32) through a
 // double-buffered, XOR-swizzled LDS tile (2 x 64 KB) that global_load_lds
 // fills directly (no register staging) while the current stage is multiplied;
 // fragment reads and loads are issued one or two at a time between the MFMAs
@@ -216,7 +216,8 @@ struct WaveGrid {
   static constexpr int kLoadsPerOperand = 256 / kWaves / 8;  // 8-row wave loads per operand
 };
 
-// Accumulate the 256x256 tile of P * Q^T into acc.  P0 points at the first
+// Accumulate the 256x256 tile of P * Q^T into acc: the fp32 kernels, on
+// v_mfma_f32_32x32x2_f32 (bf16 runs block_product16 below).  P0 points at the first
 // row of the 256-row P panel, rows K-contiguous, pitch ldp_bytes.  Q comes in
 // one of two layouts:
 //   QN == false: like P, 256 rows (j) with K contiguous (the Gram: rows of X);
@@ -244,10 +245,11 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
                                               f32x16 (&acc)[4][WaveGrid<kWaves>::kBN],
                                               BeforeLastStage&& before_last_stage,
                                               AfterLastBarrier&& after_last_barrier) {
+  static_assert(DT == kF32, "bf16 products run block_product16");
   using G = WaveGrid<kWaves>;
   constexpr int kBN = G::kBN;
   constexpr int kRowsPerWave = 256 / kWaves;
-  constexpr int EB = (DT == kBF16) ? 2 : 4;
+  constexpr int EB = 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -269,13 +271,10 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
   const uint32_t grp_p = static_cast<uint32_t>(8 * ldp_bytes);
 
   // Q offsets.  K-contiguous: as P.  Column-contiguous (QN): a stage holds
-  // kQRows rows of 256 * EB bytes (64 bf16 / 32 fp32 rows, the same K as a
-  // 128-byte K step); wave w fills rows of KB blocks 4 w .. 4 w + 3.  Row r of
-  // the stage stores logical chunk c at slot c ^ qswz(r):
-  //   bf16: qswz(r) = 4 (r & 3)       -- ds_read_b64_tr_b16 reads rows r0..r0+3
-  //                                      (r0 % 4 == 0), 64 bytes each: distinct banks
-  //   fp32: qswz(r) = 8 ((r >> 2) & 1) -- 4-byte reads of rows r and r + 4,
-  //                                      128 bytes each: distinct banks
+  // kQRows = 32 rows of 256 fp32 (the same K as a 128-byte K step); wave w
+  // fills rows of KB blocks 4 w .. 4 w + 3.  Row r of the stage stores logical
+  // chunk c at slot c ^ qswz(r), qswz(r) = 8 ((r >> 2) & 1): the 4-byte reads
+  // of rows r and r + 4, 128 bytes each, hit distinct banks.
   constexpr int kQRowBytes = 256 * EB;
   constexpr int kQRows = kOperandBytes / kQRowBytes;   // K rows per stage
   constexpr int kQRowsPerKB = 1024 / kQRowBytes;       // rows per 1 KB wave load
@@ -284,7 +283,7 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
     const int sub = lane / (64 / kQRowsPerKB);          // row within the KB block
     const int pc = lane % (64 / kQRowsPerKB);           // physical chunk in the row
     const int r0 = wave * 4 * kQRowsPerKB + sub;        // rows of load u: r0 + u * kQRowsPerKB
-    auto qswz = [](int r) { return (DT == kBF16) ? 4 * (r & 3) : 8 * ((r >> 2) & 1); };
+    auto qswz = [](int r) { return 8 * ((r >> 2) & 1); };
     offq0 = static_cast<uint32_t>(r0 * ldq_bytes + ((pc ^ qswz(r0)) << 4));
     offq1 = static_cast<uint32_t>((r0 + kQRowsPerKB) * ldq_bytes + ((pc ^ qswz(r0 + kQRowsPerKB)) << 4)) -
             static_cast<uint32_t>(kQRowsPerKB * ldq_bytes);
@@ -306,21 +305,13 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
   if constexpr (QN) {
 #pragma unroll
     for (int x = 0; x < kBN; ++x) {
+      // element e of sub-step s: row 8 s + 4 lh + e, column 32 J + li
       const int J = wc * kBN + x;
-      if constexpr (DT == kBF16) {
-        // transposed read r of sub-step s: lane reads row 16 s + 8 lh + 4 r + t,
-        // t = (lane >> 2) & 3, columns 32 J + 16 ((lane >> 4) & 1) + 4 (lane & 3) + 0..3
-        const int t = (lane >> 2) & 3;
-        qfrag[x] = (8 * lh + t) * kQRowBytes + ((4 * (J ^ t) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) << 4) +
-                   8 * (lane & 1);
-      } else {
-        // element e of sub-step s: row 8 s + 4 lh + e, column 32 J + li
-        qfrag[x] = 4 * lh * kQRowBytes + ((8 * (J ^ lh) + (li >> 2)) << 4) + 4 * (li & 3);
-      }
+      qfrag[x] = 4 * lh * kQRowBytes + ((8 * (J ^ lh) + (li >> 2)) << 4) + 4 * (li & 3);
     }
   }
 
-  using Frag = typename std::conditional<DT == kBF16, bf16x8, f32x4>::type;
+  using Frag = f32x4;
   Frag fa[2][4], fb[2][kBN];
   constexpr int kMfma = 4 * kBN;                    // MFMA blocks per sub-step
   constexpr int kReads = 4 + kBN;                   // fragment reads per sub-step
@@ -330,12 +321,6 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
     if constexpr (!QN) {
       const int co = (((2 * s + lh) ^ sw) << 4);
       fb[rs][x] = *reinterpret_cast<const Frag*>(qbase + frag_row + co + (wc * kBN + x) * 32 * 128);
-    } else if constexpr (DT == kBF16) {
-      const char* b = qbase + qfrag[x] + 16 * s * kQRowBytes;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4_ptr>((lds_cptr_t)b));
-      const bf16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4_ptr>((lds_cptr_t)(b + 4 * kQRowBytes)));
-      fb[rs][x] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     } else {
       const char* b = qbase + qfrag[x] + 8 * s * kQRowBytes;
 #pragma unroll
@@ -380,13 +365,9 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
   auto mfma_one = [&](int rs, int j) {
     if (((kMask >> j) & 1u) == 0u) return;
     const int mi = j / kBN, ni = j % kBN;
-    if constexpr (DT == kBF16) {
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[rs][ni], fa[rs][mi], acc[mi][ni], 0, 0, 0);
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[rs][ni][e], fa[rs][mi][e], acc[mi][ni], 0, 0, 0);
-    }
+    for (int e = 0; e < 4; ++e)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[rs][ni][e], fa[rs][mi][e], acc[mi][ni], 0, 0, 0);
   };
   // One sub-step: the MFMAs of register slot rs, with the next sub-step's
   // fragment reads (from (rstage, rsub) into slot rs ^ 1) and nd DMA loads
@@ -455,9 +436,228 @@ __device__ __forceinline__ void block_product(const char* __restrict__ P0, int l
 // Eight waves (two per SIMD) in a 2 x 4 grid of 128 x 64 blocks.  The load
 // maps and the update epilogue's vmcnt counts are written for this count.
 constexpr int kWaves = 8;
+// The bf16 form of block_product on v_mfma_f32_16x16x32_bf16: each wave's
+// 128 x 64 block is 8 x 4 blocks of 16 x 16, acc16[mi][ni] holding
+//   C[16 mi + (lane & 15)][16 ni + 4 (lane >> 4) + q],  q = 0..3,
+// and K advances 32 per MFMA.  At the power limit an MFMA-only loop on random
+// bf16 operands sustains 11% more flops with this shape than with 32x32x16
+// (it moves fewer accumulator registers per flop).  Loads, stages, barriers
+// and hooks are those of block_product; a 64-deep stage is two sub-steps of
+// 32, each split into two quarter-steps by P row-block halves.  Fragment reads (k = (0, 2, 1, 3)[l >> 4], the stage octet lane l's K
+// octet comes from): P (and a K-contiguous Q) lane l reads 16 bytes of row
+// 16 blk + (l & 15), logical chunk 4 s + k.  A row-major Q (QN) comes in
+// through two ds_read_b64_tr_b16 per fragment: in each 16-lane group,
+// lane 4 t + a points at K row 32 s + 8 k + 4 r + t (read r),
+// columns 16 blk + 4 a .. + 3, and receives column 16 blk + (l & 15) of those
+// four rows.  The row-major stage's swizzle qswz(r) = 4 (r & 3) ^ 2 ((r >> 4) & 1)
+// keeps the two groups a 64-bit read serves together (lanes 0..31: rows 16
+// apart) in distinct banks.
+// kMask: bit 4 mi + ni set when block (mi, ni) is needed.
+template <bool QN, unsigned kMask = 0xFFFFFFFFu, typename BeforeLastStage, typename AfterLastBarrier>
+__device__ __forceinline__ void block_product16(const char* __restrict__ P0, int ldp_bytes,
+                                                const char* __restrict__ Q0, int ldq_bytes, int kbytes, char* lds,
+                                                f32x4 (&acc)[8][4], BeforeLastStage&& before_last_stage,
+                                                AfterLastBarrier&& after_last_barrier) {
+  using G = WaveGrid<8>;
+  constexpr int kRowsPerWave = 256 / 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / G::kWN, wc = wave % G::kWN;
+
+  P0 = uniform_ptr(P0);
+  Q0 = uniform_ptr(Q0);
+  // DMA source offsets, as in block_product
+  const int lrow = lane >> 3;
+  const int lchunk0 = (lane & 7) ^ lrow;
+  const int lchunk1 = lchunk0 ^ 1;
+  const uint32_t rp = static_cast<uint32_t>((wave * kRowsPerWave + lrow) * ldp_bytes);
+  const uint32_t offp0 = rp + lchunk0 * 16, offp1 = rp + lchunk1 * 16;
+  const uint32_t grp_p = static_cast<uint32_t>(8 * ldp_bytes);
+  constexpr int kQRowBytes = 512;                     // 256 bf16 columns
+  constexpr int kQRows = kOperandBytes / kQRowBytes;  // 64 K rows per stage
+  constexpr int kQRowsPerKB = 2;
+  static_assert(kQRows == 64, "row-major stage");
+  uint32_t offq0, offq1, grp_q;
+  if constexpr (QN) {
+    // wave w fills K rows 8 w .. 8 w + 7 (KB blocks 4 w .. 4 w + 3)
+    const int sub = lane / 32, pc = lane % 32;
+    const int r0 = wave * 4 * kQRowsPerKB + sub;
+    auto qswz = [](int r) { return (4 * (r & 3)) ^ (2 * ((r >> 4) & 1)); };
+    offq0 = static_cast<uint32_t>(r0 * ldq_bytes + ((pc ^ qswz(r0)) << 4));
+    offq1 = static_cast<uint32_t>((r0 + kQRowsPerKB) * ldq_bytes + ((pc ^ qswz(r0 + kQRowsPerKB)) << 4)) -
+            static_cast<uint32_t>(kQRowsPerKB * ldq_bytes);
+    grp_q = static_cast<uint32_t>(kQRowsPerKB * ldq_bytes);
+  } else {
+    const uint32_t rq = static_cast<uint32_t>((wave * kRowsPerWave + lrow) * ldq_bytes);
+    offq0 = rq + lchunk0 * 16;
+    offq1 = rq + lchunk1 * 16;
+    grp_q = static_cast<uint32_t>(8 * ldq_bytes);
+  }
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * kRowsPerWave * 128);
+
+  // Lane group lq = lane >> 4 holds the MFMA's K octet lq; it reads the
+  // stage's octet lk = (0, 2, 1, 3)[lq] of the sub-step, the same for both
+  // operands, so each K index is still summed once.  ds_read_b128 serves
+  // lanes l and l + 32 together: with this order they read adjacent chunks
+  // of a row, which the swizzle keeps in distinct banks.
+  // K-contiguous fragment reads: row 16 blk + (lane & 15), chunk 4 s + lk
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int lk = ((lq & 1) << 1) | (lq >> 1);
+  const int frag_row = l16 * 128;
+  const int sw = (l16 & 7) ^ ((l16 >> 3) & 1);
+  // QN fragment offsets within the Q region (without the sub-step's rows), per block ni
+  int qfrag[4];
+  if constexpr (QN) {
+    const int t = (lane >> 2) & 3, a = lane & 3;
+    const int qs = (4 * t) ^ (2 * ((lk >> 1) & 1));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int ch = 8 * wc + 2 * x + (a >> 1);
+      qfrag[x] = (8 * lk + t) * kQRowBytes + ((ch ^ qs) << 4) + 8 * (a & 1);
+    }
+  }
+
+  // blocks and fragments some needed block uses
+  auto p_used = [](int mi) { return ((kMask >> (4 * mi)) & 0xFu) != 0u; };
+  auto q_used = [](int ni) { return ((kMask >> ni) & 0x11111111u) != 0u; };
+  // A 64-deep stage is four quarter-steps of 16 MFMAs: (sub-step s, half h)
+  // multiplies P row blocks 4 h .. 4 h + 3 by Q column blocks 0..3 at K
+  // 32 s .. 32 s + 31.  fb[s] holds sub-step s's Q fragments, fa[h] half h's
+  // P fragments; each quarter-step reads what the next one needs:
+  //   q0 (s0 h0): fa[1] <- sub 0 half 1
+  //   q1 (s0 h1): fb[1] <- sub 1, fa[0] <- sub 1 half 0
+  //   q2 (s1 h0): fa[1] <- sub 1 half 1
+  //   q3 (s1 h1): fb[0], fa[0] <- the next stage's sub 0 (other buffer)
+  bf16x8 fa[2][4], fb[2][4];
+  constexpr int kDma = 2 * G::kLoadsPerOperand;     // DMA loads per stage
+  auto read_q = [&](int stage, int sub, int x) {
+    if (!q_used(x)) return;
+    const char* qbase = lds + stage * kStageBytes + kOperandBytes;
+    if constexpr (!QN) {
+      const int co = (((4 * sub + lk) ^ sw) << 4);
+      fb[sub][x] = *reinterpret_cast<const bf16x8*>(qbase + frag_row + co + (wc * 4 + x) * 16 * 128);
+    } else {
+      const char* b = qbase + qfrag[x] + 32 * sub * kQRowBytes;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4_ptr>((lds_cptr_t)b));
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4_ptr>((lds_cptr_t)(b + 4 * kQRowBytes)));
+      fb[sub][x] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto read_p = [&](int stage, int sub, int h, int i) {
+    if (!p_used(4 * h + i)) return;
+    const int co = (((4 * sub + lk) ^ sw) << 4);
+    fa[h][i] = *reinterpret_cast<const bf16x8*>(lds + stage * kStageBytes + frag_row + co +
+                                                (wr * 8 + 4 * h + i) * 16 * 128);
+  };
+  auto dma_one = [&](int stage, int kb, int i) {
+    const uint32_t dp = lds_wave + stage * kStageBytes;
+    const int u = i >> 1;
+    if ((i & 1) == 0) {
+      lds_dma16(P0, ((u & 1) ? offp1 : offp0) + u * grp_p + kb, dp + u * 1024);
+    } else if constexpr (QN) {
+      const char* qk = Q0 + static_cast<long>(kb >> 7) * kQRows * static_cast<long>(ldq_bytes);
+      lds_dma16(qk, ((u & 1) ? offq1 : offq0) + u * grp_q, dp + kOperandBytes + u * 1024);
+    } else {
+      lds_dma16(Q0, ((u & 1) ? offq1 : offq0) + u * grp_q + kb, dp + kOperandBytes + u * 1024);
+    }
+  };
+  auto mfma_one = [&](int s, int h, int j) {
+    const int mi = 4 * h + j / 4, ni = j % 4;
+    if (((kMask >> (4 * mi + ni)) & 1u) == 0u) return;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[s][ni], fa[h][j / 4], acc[mi][ni], 0, 0, 0);
+  };
+  // One quarter-step: its 16 MFMAs with nr reads (rd(0) .. rd(nr - 1)) and nd
+  // DMA loads spread between them, each group pinned in place.
+  auto quarter = [&](int s, int h, auto&& rd, int nr, auto&& dma, int nd) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_one(s, h, j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = j * nr / 16; i < (j + 1) * nr / 16; ++i) rd(i);
+#pragma unroll
+      for (int i = j * nd / 16; i < (j + 1) * nd / 16; ++i) dma(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto no_dma = [](int) {};
+  // the reads each quarter-step issues; the next stage's sub-step 0 comes
+  // from buffer nc: Q fragments first, in the order the MFMAs use them
+  auto rd_q0 = [&](int c) { return [&, c](int i) { read_p(c, 0, 1, i); }; };
+  auto rd_q1 = [&](int c) { return [&, c](int i) { if (i < 4) read_q(c, 1, i); else read_p(c, 1, 0, i - 4); }; };
+  auto rd_q2 = [&](int c) { return [&, c](int i) { read_p(c, 1, 1, i); }; };
+  auto rd_q3 = [&](int nc) { return [&, nc](int i) { if (i < 4) read_q(nc, 0, i); else read_p(nc, 0, 0, i - 4); }; };
+  auto no_rd = [](int) {};
+
+  // Pipeline: stage kt is multiplied from buffer kt & 1 while stage kt + 1
+  // lands in the other buffer.  After quarter-step 2 every read of buffer
+  // kt & 1 has been issued; the barrier retires them, and quarter-step 3
+  // issues stage kt + 2's loads into that buffer, which have until the barrier
+  // after the next stage's quarter-step 2 to land.  The buffer stage nk - 2
+  // frees receives the caller's early loads instead (before_last_stage).
+  const int nk = kbytes / 128;
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) dma_one(0, 0, i);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) dma_one(1, 128, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rd_q3(0)(i);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt < nk - 2; ++kt) {
+    const int c = kt & 1;
+    quarter(0, 0, rd_q0(c), 4, no_dma, 0);
+    quarter(0, 1, rd_q1(c), 8, no_dma, 0);
+    quarter(1, 0, rd_q2(c), 4, no_dma, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    quarter(1, 1, rd_q3(c ^ 1), 8, [&](int i) { dma_one(c, (kt + 2) * 128, i); }, kDma);
+  }
+  // stage nk - 2: buffer 0 is free after its barrier
+  quarter(0, 0, rd_q0(0), 4, no_dma, 0);
+  quarter(0, 1, rd_q1(0), 8, no_dma, 0);
+  quarter(1, 0, rd_q2(0), 4, no_dma, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  quarter(1, 1, rd_q3(1), 8, before_last_stage, kDma);
+  // final stage: no more loads; after its barrier nothing reads the operand
+  // buffers again, so the caller may start filling LDS while the last
+  // quarter-step's MFMAs run
+  quarter(0, 0, rd_q0(1), 4, no_dma, 0);
+  quarter(0, 1, rd_q1(1), 8, no_dma, 0);
+  quarter(1, 0, rd_q2(1), 4, no_dma, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  after_last_barrier();
+  quarter(1, 1, no_rd, 0, no_dma, 0);
+}
+
+
 using Grid = WaveGrid<kWaves>;
 constexpr int kBN = Grid::kBN;
 constexpr int kThreads = Grid::kThreadsPerBlock;
+
+// Per-wave accumulators: bf16 on 16 x 16 MFMA blocks (block_product16), fp32
+// on 32 x 32 ones (block_product).  Both are 128 floats per lane.
+template <int DT> struct AccOf { using type = f32x16[4][kBN]; };
+template <> struct AccOf<kBF16> { using type = f32x4[8][4]; };
+template <int DT> using Acc = typename AccOf<DT>::type;
+template <int DT> __device__ __forceinline__ void zero_acc(Acc<DT>& acc) {
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{};
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
+  }
+}
 
 // ---------------------------------------------------------------- epilogue
 // The MFMAs take (Q, P) so each accumulator block holds the transposed
@@ -490,6 +690,21 @@ __device__ __forceinline__ void stage_acc(char* lds, const f32x16 (&acc)[4][kBN]
                                      acc[mi][ni][4 * g + 2] * scale, acc[mi][ni][4 * g + 3] * scale);
         *reinterpret_cast<float4*>(lds + stage_off(32 * mi + li, cbase + 8 * ni + 2 * g + lh)) = v;
       }
+}
+
+// The same from 16 x 16 blocks: lane l of block (mi, ni) holds row
+// 16 mi + (l & 15), columns 16 ni + 4 (l >> 4) .. + 3 of the wave's block.
+__device__ __forceinline__ void stage_acc(char* lds, const f32x4 (&acc)[8][4], float scale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cbase = (wave % Grid::kWN) * kBN * 8;
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const f32x4& a = acc[mi][ni];
+      *reinterpret_cast<float4*>(lds + stage_off(16 * mi + (lane & 15), cbase + 4 * ni + (lane >> 4))) =
+          make_float4(a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale);
+    }
 }
 
 __device__ __forceinline__ float4 stage_ld4(const char* lds, int r, int c) {
@@ -604,6 +819,25 @@ __device__ __forceinline__ void store_partial(float* part, const f32x16 (&acc)[4
       }
 }
 
+__device__ __forceinline__ void store_partial(float* part, const f32x4 (&acc)[8][4]) {
+  f32v4* dst = reinterpret_cast<f32v4*>(part) + threadIdx.x;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const f32x4& a = acc[b >> 2][b & 3];
+    *gmem(dst + b * kThreads) = f32v4{a[0], a[1], a[2], a[3]};
+  }
+}
+
+__device__ __forceinline__ void add_partial(const float* part, f32x4 (&acc)[8][4]) {
+  const f32v4* src = reinterpret_cast<const f32v4*>(part) + threadIdx.x;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const f32v4 v = *gmem(src + b * kThreads);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[b >> 2][b & 3][e] += v[e];
+  }
+}
+
 __device__ __forceinline__ void add_partial(const float* part, f32x16 (&acc)[4][kBN]) {
   const f32v4* src = reinterpret_cast<const f32v4*>(part) + threadIdx.x;
 #pragma unroll
@@ -638,31 +872,37 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   // tile whole)
   const bool diag = tr.bi == tr.bj && !tr.full;
 
-  f32x16 acc[4][kBN];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
+  Acc<DT> acc;
+  zero_acc<DT>(acc);
 
   if (!reduce) {
     // K slice of this block: all of K, or 1 / ksplit of it (a multiple of 256)
     const int klen = kdim / tr.ksplit;
     const char* p = xs + static_cast<long>(tr.bi) * kTile * ld + static_cast<long>(tr.slice) * klen * EB;
     const char* q = xs + static_cast<long>(tr.bj) * kTile * ld + static_cast<long>(tr.slice) * klen * EB;
-    // A diagonal tile needs only its 32 x 32 blocks on or below the block
-    // diagonal: the epilogue writes the others as transposes.  Block (R, C)
-    // of the tile (R = 4 wr + mi, C = kBN wc + ni) is needed when C <= R, so
-    // each wave runs one of four patterns (Grid: 2 x 4 waves of 4 x 2 blocks)
+    // A diagonal tile needs only its MFMA blocks on or below the block
+    // diagonal: the epilogue writes the others as transposes.  Each wave runs
+    // one of four patterns (Grid: 2 x 4 waves).  bf16, 16 x 16 blocks: block
+    // (R, C) = (8 wr + mi, 4 wc + ni), needed when C <= R.  fp32, 32 x 32
+    // blocks: (4 wr + mi, 2 wc + ni).
     static_assert(Grid::kWN == 4 && kBN == 2, "diagonal block patterns");
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int band = (wv % Grid::kWN) - 2 * (wv / Grid::kWN);   // wave column pair relative to its row band
     auto run = [&](auto mask) {
-      block_product<DT, kWaves, false, decltype(mask)::value>(p, ld, q, ld, klen * EB, lds, acc, [](int) {}, [] {});
+      if constexpr (DT == kBF16)
+        block_product16<false, decltype(mask)::value>(p, ld, q, ld, klen * EB, lds, acc, [](int) {}, [] {});
+      else
+        block_product<DT, kWaves, false, decltype(mask)::value>(p, ld, q, ld, klen * EB, lds, acc, [](int) {},
+                                                                [] {});
     };
-    if (!diag || band < 0) run(std::integral_constant<unsigned, 0xFFu>{});        // below the diagonal
-    else if (band == 0) run(std::integral_constant<unsigned, 0xFDu>{});           // all but block (0, 1)
-    else if (band == 1) run(std::integral_constant<unsigned, 0xD0u>{});           // blocks (2, 0), (3, 0), (3, 1)
-    else run(std::integral_constant<unsigned, 0x00u>{});                          // above the diagonal
+    constexpr bool k16 = DT == kBF16;
+    using All = std::integral_constant<unsigned, k16 ? 0xFFFFFFFFu : 0xFFu>;
+    using OnDiag = std::integral_constant<unsigned, k16 ? 0xFFFFF731u : 0xFDu>;     // C <= R within the wave
+    using RightOfDiag = std::integral_constant<unsigned, k16 ? 0xF7310000u : 0xD0u>;
+    if (!diag || band < 0) run(All{});                  // below the diagonal
+    else if (band == 0) run(OnDiag{});
+    else if (band == 1) run(RightOfDiag{});
+    else run(std::integral_constant<unsigned, 0u>{});   // above the diagonal
     if (tr.ksplit > 1) {
       store_partial(tr.part + static_cast<long>(tr.slice) * kPartialFloats, acc);
       return;
@@ -679,10 +919,11 @@ __global__ __launch_bounds__(kThreads, 1) void syrk_kernel(const MatDesc* __rest
   const int Rt = tr.bi * kTile, Ct = tr.bj * kTile;
   const bool mirror = tr.bi != tr.bj && !tr.full;
   __syncthreads();  // operand stages are free
-  // A diagonal tile holds its 32 x 32 blocks on and below the block diagonal:
+  // A diagonal tile holds its MFMA blocks on and below the block diagonal:
   // rows write only those, and every strictly-lower block is also written
-  // transposed, which fills the rest.  blk(x) = x / 32.
-  auto upper = [&](int row, int col) { return diag && (col >> 5) > (row >> 5); };
+  // transposed, which fills the rest.  blk(x) = x / 16 (bf16) or x / 32.
+  constexpr int kBlkShift = (DT == kBF16) ? 4 : 5;
+  auto upper = [&](int row, int col) { return diag && (col >> kBlkShift) > (row >> kBlkShift); };
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     if (wr == h) stage_acc(lds, acc, alpha);
@@ -745,11 +986,8 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   T* xs_next = static_cast<T*>((step & 1) ? d.xs0 : d.xs1);
   const long lda = static_cast<long>(mp) * EB;
 
-  f32x16 acc[4][kBN];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kBN; ++ni) acc[mi][ni] = f32x16{};
+  Acc<DT> acc;
+  zero_acc<DT>(acc);
 
   const float gamma = (step == 0) ? scales[tr.mat].c : 1.0f;
   const int tid = threadIdx.x, wr = (tid >> 6) / Grid::kWN;
@@ -810,34 +1048,55 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
   // quarter 0 lands in the buffer the second-to-last stage frees, a stage
   // before the product ends; quarter 1 starts at the last barrier
   static_assert(kDmaRows == 2 * Grid::kLoadsPerOperand, "one early load per main-loop DMA slot");
-  block_product<DT, kWaves, true>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
-                                  xq + static_cast<long>(tr.bj) * kTile * EB, np * EB, mp * EB, lds, acc,
-                                  [&](int i) { dma_quarter_row(0, i); }, [&] { dma_quarter(1); });
+  if constexpr (DT == kBF16)
+    block_product16<true>(a + static_cast<long>(tr.bi) * kTile * lda, lda, xq + static_cast<long>(tr.bj) * kTile * EB,
+                          np * EB, mp * EB, lds, acc, [&](int i) { dma_quarter_row(0, i); }, [&] { dma_quarter(1); });
+  else
+    block_product<DT, kWaves, true>(a + static_cast<long>(tr.bi) * kTile * lda, lda,
+                                    xq + static_cast<long>(tr.bj) * kTile * EB, np * EB, mp * EB, lds, acc,
+                                    [&](int i) { dma_quarter_row(0, i); }, [&] { dma_quarter(1); });
   wait_vmcnt<kDmaRows>();
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     char* buf = lds + (q & 1) * kQBytes;
-    {
+    if constexpr (DT == kBF16) {
+      // quarter q is 16 x 16 blocks mi = 2 q + m2 of every wave: lane l holds
+      // buffer row 32 wr + 16 m2 + (l & 15), columns 4 c4 .. 4 c4 + 3 with
+      // c4 = cbase + 4 ni + (l >> 4), i.e. half (l >> 4) & 1 of chunk pair
+      // (c4 & ~1, c4 | 1).  All reads of the block first, then the updates.
+      const int l16 = lane & 15, lq = lane >> 4;
+      float4 xv[2][4];
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int r = 32 * wr + 16 * m2 + l16, c4 = cbase + 4 * ni + lq;
+          const bf16x4 h = *reinterpret_cast<const bf16x4*>(buf + stage_off(r, c4 & ~1) + 8 * (lq & 1));
+          const bf16x4 l = *reinterpret_cast<const bf16x4*>(buf + stage_off(r, c4 | 1) + 8 * (lq & 1));
+          xv[m2][ni] = make_float4(static_cast<float>(h[0]) + static_cast<float>(l[0]),
+                                   static_cast<float>(h[1]) + static_cast<float>(l[1]),
+                                   static_cast<float>(h[2]) + static_cast<float>(l[2]),
+                                   static_cast<float>(h[3]) + static_cast<float>(l[3]));
+        }
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const float4 x = xv[m2][ni];
+          const f32x4& ax = acc[2 * q + m2][ni];
+          *reinterpret_cast<float4*>(buf + stage_off(32 * wr + 16 * m2 + l16, cbase + 4 * ni + lq)) =
+              make_float4(gamma * (cx * x.x + cax * ax[0]), gamma * (cx * x.y + cax * ax[1]),
+                          gamma * (cx * x.z + cax * ax[2]), gamma * (cx * x.w + cax * ax[3]));
+        }
+    } else {
       // all reads of the block first, then the updates (one LDS round trip)
       float4 xv[kBN][4];
 #pragma unroll
       for (int ni = 0; ni < kBN; ++ni)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r = 32 * wr + li, c4 = cbase + 8 * ni + 2 * g + lh;
-          if constexpr (DT == kBF16) {
-            // columns 4 c4 .. 4 c4 + 3: half lh of chunk pair (c4 & ~1, c4 | 1)
-            const bf16x4 h = *reinterpret_cast<const bf16x4*>(buf + stage_off(r, c4 & ~1) + 8 * lh);
-            const bf16x4 l = *reinterpret_cast<const bf16x4*>(buf + stage_off(r, c4 | 1) + 8 * lh);
-            xv[ni][g] = make_float4(static_cast<float>(h[0]) + static_cast<float>(l[0]),
-                                    static_cast<float>(h[1]) + static_cast<float>(l[1]),
-                                    static_cast<float>(h[2]) + static_cast<float>(l[2]),
-                                    static_cast<float>(h[3]) + static_cast<float>(l[3]));
-          } else {
-            xv[ni][g] = *reinterpret_cast<const float4*>(buf + stage_off(r, c4));
-          }
-        }
+        for (int g = 0; g < 4; ++g)
+          xv[ni][g] = *reinterpret_cast<const float4*>(buf + stage_off(32 * wr + li, cbase + 8 * ni + 2 * g + lh));
 #pragma unroll
       for (int ni = 0; ni < kBN; ++ni)
 #pragma unroll
