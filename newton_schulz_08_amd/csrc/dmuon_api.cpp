@@ -1315,10 +1315,10 @@ const char* dmuon_last_error(void) { return g_last_error.c_str(); }
 const char* dmuon_backend_info(void) {
   return "dmuon gfx950 | prologue: fused momentum/Nesterov/Frobenius partials, 16x256 tiles (64x64 with an"
          " LDS transpose for tall matrices) | syrk: lower-triangle 256x256 tiles + transposed mirror,"
-         " v_mfma_f32_32x32x16_bf16 / 32x32x2_f32 | ns_gemm: 256x256 tiles, X read row-major through"
+         " v_mfma_f32_16x16x32_bf16 / 32x32x2_f32 | ns_gemm: 256x256 tiles, X read row-major through"
          " ds_read_b64_tr_b16, fused c0 X + c1 A X epilogue (cubic 1.5/-0.5 by default; three-term maps"
          " add a c2 A^2 + c1 A square launch), bf16 iterate kept as a hi/lo pair, last step writes"
-         " p = p (1 - lr wd) - lr s U"
+         " p = p (1 - lr wd) - lr s U | fp32 with m' <= 512: 128x128 tiles"
          " | ragged batch: shape-grouped segments, per-XCD balanced tile shares | built " __DATE__;
 }
 
