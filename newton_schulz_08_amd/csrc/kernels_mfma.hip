@@ -7,8 +7,9 @@
 //   syrk_kernel    A = alpha * X X^T      lower-triangle 256x256 tiles only; each
 //                                         off-diagonal tile is also stored
 //                                         transposed into the upper triangle, and
-//                                         a diagonal tile's upper-right quadrant
-//                                         is its lower-left one transposed.
+//                                         a diagonal tile computes only its MFMA
+//                                         blocks on or below the diagonal and
+//                                         stores the others as their transposes.
 //   ns_gemm_kernel X <- g * (c0 X + c1 A X)    fused epilogue (blog's cubic map:
 //                                         c0 = 1.5, c1 = -0.5); on the last step
 //                                         it writes the update into the caller's
@@ -206,7 +207,8 @@ __device__ __forceinline__ void lds_dma16_addr_nt(const void* src, uint32_t lds_
 template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Wave grid of a 256x256 tile: 2 waves along M (128 rows each) and
-// kWaves / 2 along N; each wave owns kBM x kBN blocks of 32x32.
+// kWaves / 2 along N; each wave owns kBM x kBN blocks of 32x32 (the fp32 MFMA
+// shape; bf16 splits each into 2 x 2 blocks of 16x16).
 template <int kWaves>
 struct WaveGrid {
   static constexpr int kThreadsPerBlock = 64 * kWaves;
