@@ -119,6 +119,37 @@ def test_ragged_batch(dtype):
     print(f"ragged {dtype}: worst NS rel err {worst:.3e}", flush=True)
 
 
+def _random_shapes(seed, n=24):
+    """Seeded shapes across the cases the plan distinguishes: tiny and odd
+    sizes, each side of the 256 tile and the 512 small-tile bounds, log-uniform
+    sizes up to 1200 in both orientations (numel < 100000 takes the
+    elementwise route)."""
+    rng = np.random.default_rng(seed)
+    edges = [255, 256, 257, 511, 512, 513]
+    shapes = []
+    for i in range(n):
+        if i < 4:
+            a, b = (int(x) for x in rng.integers(1, 41, size=2))
+        elif i < 10:
+            a, b = edges[i - 4], int(rng.integers(200, 1101))
+        else:
+            a, b = (int(x) for x in np.exp(rng.uniform(np.log(24.0), np.log(1200.0), size=2)).round())
+        shapes.append((a, b) if rng.integers(2) else (b, a))
+    return shapes
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_random_shapes(dtype):
+    """One call over 24 seeded shapes of every kind at once (both routes, both
+    orientations, ragged and tile-edge sizes); every matrix against the oracle."""
+    shapes = _random_shapes(2024 if dtype == "f32" else 2025)
+    print(f"random shapes {dtype}: {shapes}", flush=True)
+    cfg = _adhoc(shapes, dtype, 140 + (dtype == "bf16"))
+    res = run_muon(cfg, nonzero_buf=True)
+    worst = check_against_oracle(cfg, res)
+    print(f"random shapes {dtype}: worst NS rel err {worst:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("nesterov", [True, False])
 def test_nonzero_momentum_and_lr_scale(dtype, nesterov):
