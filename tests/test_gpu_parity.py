@@ -333,6 +333,24 @@ def test_ns_batched_ragged(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ns_steps", [3, 7])
+def test_ns_batched_random_shapes(dtype, ns_steps):
+    """Newton-Schulz alone (every matrix orthogonalised, tiny ones included)
+    over 24 seeded shapes in one call, each against the oracle."""
+    shapes = _random_shapes(3000 + ns_steps + 10 * (dtype == "bf16"))
+    cfg = _adhoc(shapes, dtype, 180 + ns_steps + 10 * (dtype == "bf16"))
+    xs = [gen.draw_matrix(cfg, i, gen.GRAD) for i in range(len(shapes))]
+    outs = nsa.ns_batched([to_device(x) for x in xs], ns_steps=ns_steps)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for x, o, sh in zip(xs, outs, shapes):
+        err = rel_fro(to_host_f64(o), oracle.newton_schulz(x.as_f64(), ns_steps))
+        assert err <= TOL[dtype], (sh, err)
+        worst = max(worst, err)
+    print(f"ns_batched random shapes {dtype} k={ns_steps}: worst rel err {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_full_gram_ablation_matches(dtype, monkeypatch):
     """DMUON_NS_KERNEL=gemm (every Gram tile, no mirror) gives the default
     path's result to rounding and meets the oracle tolerance."""
