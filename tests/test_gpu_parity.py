@@ -463,6 +463,18 @@ def test_muon_step_quintic_with_decay(dtype):
     check_against_oracle(cfg, res, weight_decay=0.05, ns_coeffs=QUINTIC_FAST)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_three_term_random_shapes(dtype):
+    """The three-term map (the square launch B = c2 A A + c1 A, split into K
+    slices for small matrices) with the classical quintic over 24 seeded
+    shapes, every matrix against the oracle."""
+    shapes = _random_shapes(4000 + (dtype == "bf16"))
+    cfg = _adhoc(shapes, dtype, 230 + (dtype == "bf16"))
+    res = run_muon(cfg, ns_coeffs=QUINTIC_CLASSICAL)
+    worst = check_against_oracle(cfg, res, ns_coeffs=QUINTIC_CLASSICAL)
+    print(f"three-term random shapes {dtype}: worst NS rel err {worst:.3e}", flush=True)
+
+
 def test_ns_batched_in_place():
     x = torch.randn(384, 896, device="cuda")
     ref = nsa.ns_batched([x.clone()], ns_steps=5)[0]
