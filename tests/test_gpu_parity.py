@@ -120,7 +120,7 @@ def test_ragged_batch(dtype):
 
 
 def _random_shapes(seed, n=24):
-    """Seeded shapes across the cases the plan distinguishes: tiny and odd
+    """Seeded shapes across the cases the launch planner distinguishes: tiny and odd
     sizes, each side of the 256 tile and the 512 small-tile bounds, log-uniform
     sizes up to 1200 in both orientations (numel < 100000 takes the
     elementwise route)."""
