@@ -1193,9 +1193,9 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_kernel(const MatDesc* __r
 // the blocks): four waves in a 2 x 2 grid of 64 x 64 blocks, each 2 x 2
 // v_mfma_f32_32x32x2_f32 blocks.  An fp32 MFMA occupies its SIMD for 64 cycles,
 // so register-staged loads into padded LDS rows keep it fed.  The epilogues
-// work straight from the
-// accumulators (lane (li, lh), register 4 g + q of block (mi, ni) is
-// C[64 wr + 32 mi + li][64 wc + 32 ni + 8 g + 4 lh + q], as above).
+// work straight from the accumulators (lane (li, lh), register 4 g + q of
+// block (mi, ni) is C[64 wr + 32 mi + li][64 wc + 32 ni + 8 g + 4 lh + q], as
+// above).
 constexpr int kSmThreads = 256;
 // K per stage: two stages of 16 take 40 KB of LDS and at most 128 VGPRs, so
 // four workgroups share a CU and the TinyMLP set's 768 update tiles are all
